@@ -1,0 +1,124 @@
+"""Host-side ring schedule for one device's share of a ring-attention prefill.
+
+Context parallelism cuts each prompt along the sequence into N contiguous
+chunks, one per device; with Ring Attention every device keeps its query
+chunk and runs attention on each key/value chunk as it arrives from its ring
+neighbour (Moreh, "Optimizing Long-Context Prefill on Multiple
+Older-Generation GPU Nodes", section "Introduction to Context Parallelism":
+the context-parallelism paragraph and the Ring Attention bullet).  At step t
+device r holds the chunk that started on device (r - t) mod N.
+
+On one GPU the ring is simulated: all key/value chunks are already resident
+in HBM and the "arrival" of chunk j is simply its turn in the loop.  This
+module only does index arithmetic and calls the library; every step of the
+computation runs in the HIP kernels.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _native
+
+
+@dataclass(frozen=True)
+class RingLayout:
+    """Packed sequences, each cut into ``n_chunks`` equal contiguous chunks."""
+
+    seqlens: tuple
+    n_chunks: int
+
+    def __post_init__(self):
+        for n in self.seqlens:
+            if n % self.n_chunks:
+                raise ValueError(f"sequence length {n} does not split into {self.n_chunks} chunks")
+
+    @property
+    def chunk_lens(self):
+        return [n // self.n_chunks for n in self.seqlens]
+
+    @property
+    def cu(self):
+        """Prefix offsets of one chunk in packed form (the same for every chunk)."""
+        out = [0]
+        for c in self.chunk_lens:
+            out.append(out[-1] + c)
+        return out
+
+    def pos0(self, chunk: int):
+        """Global position of each sequence's first token in chunk ``chunk``."""
+        return [chunk * c for c in self.chunk_lens]
+
+    def ranges(self, chunk: int):
+        """Row ranges (start, stop) of chunk ``chunk`` inside the full packed tensor."""
+        out, start = [], 0
+        for n, c in zip(self.seqlens, self.chunk_lens):
+            out.append((start + chunk * c, start + (chunk + 1) * c))
+            start += n
+        return out
+
+    def gather(self, x: torch.Tensor, chunk: int) -> torch.Tensor:
+        """Chunk ``chunk`` of packed tensor ``x`` in packed form (a view for one sequence)."""
+        parts = [x[a:b] for a, b in self.ranges(chunk)]
+        return parts[0] if len(parts) == 1 else torch.cat(parts, dim=0)
+
+    def visible_pairs(self, rank: int) -> int:
+        """Causal (query, key) pairs whose query is in chunk ``rank``."""
+        total = 0
+        for c in self.chunk_lens:
+            lo, hi = rank * c, (rank + 1) * c
+            total += (hi * (hi + 1) - lo * (lo + 1)) // 2
+        return total
+
+
+def ring_chunk(rank: int, step: int, n_chunks: int) -> int:
+    """Key/value chunk that device ``rank`` holds at ring step ``step``."""
+    return (rank - step) % n_chunks
+
+
+class RingAttention:
+    """Runs device ``rank``'s ring: N steps of attention and LSE merges into (o, lse).
+
+    ``q_local`` is the device's packed query chunk; ``kv_chunks[j]`` is the
+    packed (k, v) of chunk j, already in device memory.  The first step that
+    has visible keys writes straight into the running state (merging into the
+    identity would give the same bits); every later active step writes the
+    partial buffers and is folded in by ``attn_ring_merge``.  Fully masked
+    steps launch nothing.
+    """
+
+    def __init__(self, layout: RingLayout, rank: int, scale: float = 0.0):
+        if not 0 <= rank < layout.n_chunks:
+            raise ValueError("rank outside the ring")
+        self.layout = layout
+        self.rank = rank
+        self.scale = scale
+
+    def run(self, q_local, kv_chunks, o_acc, lse_acc, o_part, lse_part, stream=None) -> int:
+        lay, r = self.layout, self.rank
+        cu = lay.cu
+        q_pos0 = lay.pos0(r)
+        wrote_state = False
+        active = 0
+        for t in range(lay.n_chunks):
+            j = ring_chunk(r, t, lay.n_chunks)
+            k_j, v_j = kv_chunks[j]
+            dst = (o_part, lse_part) if wrote_state else (o_acc, lse_acc)
+            launched = _native.attn_ring_step(q_local, k_j, v_j, *dst, cu_q=cu, cu_k=cu,
+                                              q_pos0=q_pos0, k_pos0=lay.pos0(j),
+                                              scale=self.scale, causal=True, report_skip=True,
+                                              stream=stream)
+            if not launched:
+                continue
+            active += 1
+            if wrote_state:
+                _native.attn_ring_merge(o_acc, lse_acc, o_part, lse_part, stream=stream)
+            wrote_state = True
+        if not wrote_state:  # every chunk was in the future: the state is the identity
+            k_j, v_j = kv_chunks[ring_chunk(r, 0, lay.n_chunks)]
+            _native.attn_ring_step(q_local, k_j, v_j, o_acc, lse_acc, cu_q=cu, cu_k=cu,
+                                   q_pos0=q_pos0, k_pos0=lay.pos0(r), scale=self.scale,
+                                   causal=True, report_skip=False, stream=stream)
+        return active
