@@ -1,0 +1,288 @@
+"""Throughput of one device's share of ring-attention prefill on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for the ring workloads, the device's N ring steps (attention of its query
+chunk against every key/value chunk, fully masked chunks skipped) and the LSE
+merges; for the prefill workload, one full causal attention call.  Inputs
+are resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is algorithmic TFLOP/s: 4 * head_dim * Hq
+flops per causal (query, key) pair (2*d for the score, 2*d for the weighted
+sum of values); masked work and softmax arithmetic are not counted.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload ring_64k_rank7]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal GQA prefill attention TFLOP/s & % bf16 peak at 32K/64K/100K, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
+DOMINANT_KERNEL = "fwd_bf16_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16.json")
+KERNEL_SOURCES = ["fwd_bf16.hip", "kernels.h"]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ring_64k_rank7")
+    ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,varlen_ulysses_rank7",
+                    help="comma list of further workloads measured in the same run ('' for none)")
+    ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=384,
+                    help="query rows of the oracle sample (all heads, all ring steps)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (for counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ring_attention_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Job:
+    """One workload with its inputs resident on the device and a run() for one step."""
+
+    def __init__(self, name):
+        import torch
+
+        from ring_attention_03_amd import RingAttention, RingLayout
+        from ring_attention_03_amd.workloads import WORKLOADS, make_qkv
+
+        self.w = w = WORKLOADS[name]
+        self.name = name
+        q, k, v = make_qkv(w)
+        self.cpu_inputs = (q, k, v)
+        dev = torch.device("cuda:0")
+        self.layout = RingLayout(w.seqlens, w.n_chunks)
+        self.rank = 0 if w.rank is None else w.rank
+        lay = self.layout
+        if w.n_chunks == 1:
+            self.q = q.to(dev)
+            self.k, self.v = k.to(dev), v.to(dev)
+            self.cu = lay.cu
+        else:
+            self.q = lay.gather(q, self.rank).to(dev).contiguous()
+            self.chunks = [(lay.gather(k, j).to(dev).contiguous(), lay.gather(v, j).to(dev).contiguous())
+                           for j in range(w.n_chunks)]
+            self.ring = RingAttention(lay, self.rank)
+        tq, hq, d = self.q.shape
+        self.o = torch.empty(tq, hq, d, device=dev)
+        self.lse = torch.empty(hq, tq, device=dev)
+        if w.n_chunks > 1:
+            self.o_p, self.lse_p = torch.empty_like(self.o), torch.empty_like(self.lse)
+        self.pairs = lay.visible_pairs(self.rank)
+        self.flops = 4 * w.head_dim * w.num_q_heads * self.pairs
+
+    def run(self, events=None):
+        from ring_attention_03_amd import attn_prefill_causal
+
+        if self.w.n_chunks == 1:
+            if events is None:
+                attn_prefill_causal(self.q, self.k, self.v, self.o, self.lse, cu_seqlens=self.cu)
+            else:
+                import torch
+
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                attn_prefill_causal(self.q, self.k, self.v, self.o, self.lse, cu_seqlens=self.cu)
+                e.record()
+                events.append(("step", s, e))
+            return 1
+        return self.ring.run(self.q, self.chunks, self.o, self.lse, self.o_p, self.lse_p, events=events)
+
+    def config(self):
+        w = self.w
+        return {"workload": self.name, "seq_lens": list(w.seqlens), "ring_chunks": w.n_chunks,
+                "rank": self.rank, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                "head_dim": w.head_dim, "causal": True, "local_q_rows": int(self.q.shape[0]),
+                "algorithmic_tflop": self.flops / 1e12}
+
+
+def time_job(job, steps, warmup):
+    """Median-free whole-job timing: warmup, then exactly `steps` steps between synchronizations.
+
+    Per-kernel durations come from HIP events recorded around every launch on
+    the launch stream during the same timed steps.
+    """
+    import torch
+
+    for _ in range(warmup):
+        job.run()
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        job.run(events=events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kind = {}
+    for kind, s, e in events:
+        per_kind.setdefault(kind, []).append(s.elapsed_time(e))
+    return wall, per_kind
+
+
+def summarize(job, steps, wall, per_kind):
+    ms = wall * 1e3 / steps
+    tflops = job.flops / (ms * 1e-3) / 1e12
+    step_ms = per_kind.get("step", [])
+    merge_ms = per_kind.get("merge", [])
+    out = {"ms_per_step": ms, "tflops": tflops, "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+           "step_launches_per_step": len(step_ms) / steps,
+           "step_kernel_ms_avg": (sum(step_ms) / len(step_ms)) if step_ms else None,
+           "merge_kernel_ms_avg": (sum(merge_ms) / len(merge_ms)) if merge_ms else None}
+    if step_ms:
+        # all algorithmic flops are done by the attention launches
+        out["attention_kernel_tflops"] = job.flops * steps / (sum(step_ms) * 1e-3) / 1e12
+    return out
+
+
+def traffic_entry(job):
+    """HBM bytes per attention launch from committed counter runs, if they match this kernel build."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_hash() or rec.get("workload") != job.name:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(job, nrows):
+    """The fp64 oracle timed on host cores for a seeded sample of the device's rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import causal_attention_ref, ring_ref
+    from ring_attention_03_amd.workloads import sample_rows
+
+    w = job.w
+    q, k, v = job.cpu_inputs
+    local_rows = int(job.q.shape[0])
+    rows = sample_rows(local_rows, nrows, w.seed)[:nrows]
+    t0 = time.perf_counter()
+    if w.n_chunks == 1:
+        causal_attention_ref(q, k, v, w.seqlens, rows=rows)
+    else:
+        ring_ref(q, k, v, w.seqlens, w.n_chunks, job.rank, rows=rows)
+    sec = time.perf_counter() - t0
+    # work of the sampled rows: each local row sees its global position + 1 keys
+    cl = job.layout.chunk_lens
+    cu = np.cumsum([0] + cl)
+    pairs = 0
+    for r in rows:
+        b = int(np.searchsorted(cu, r, side="right") - 1)
+        pairs += job.rank * cl[b] + (r - cu[b]) + 1
+    flops = 4 * w.head_dim * w.num_q_heads * pairs
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {local_rows} local query rows (first/last 8 + seeded random), "
+                      f"all {w.num_q_heads} heads, full ring; fp64 numpy; {sec:.1f} s, "
+                      f"{flops / 1e9:.1f} GFLOP algorithmic; host {cpu}, os.cpu_count()={os.cpu_count()}"}
+
+
+def calibrate_copy(mib):
+    import torch
+
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
+              "(the ring across GPUs is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    from ring_attention_03_amd import load_library
+
+    load_library()
+    log = lambda m: print(m, file=sys.stderr, flush=True)  # noqa: E731
+
+    log(f"bench: preparing {args.workload}")
+    job = Job(args.workload)
+    wall, per_kind = time_job(job, args.steps, args.warmup)
+    main_res = summarize(job, args.steps, wall, per_kind)
+    log(f"bench: {args.workload}: {main_res['ms_per_step']:.3f} ms/step, {main_res['tflops']:.1f} TFLOP/s "
+        f"({main_res['pct_bf16_peak']:.1f}% of bf16 peak)")
+
+    extra = {}
+    for name in [x for x in args.extra.split(",") if x and x != args.workload]:
+        log(f"bench: preparing {name}")
+        ej = Job(name)
+        ew, epk = time_job(ej, args.extra_steps, 1)
+        extra[name] = summarize(ej, args.extra_steps, ew, epk)
+        extra[name]["algorithmic_tflop"] = ej.flops / 1e12
+        log(f"bench: {name}: {extra[name]['ms_per_step']:.3f} ms/step, {extra[name]['tflops']:.1f} TFLOP/s")
+        del ej
+        torch.cuda.empty_cache()
+
+    achieved = main_res.get("attention_kernel_tflops")
+    traffic = traffic_entry(job)
+    roofline = {"bound": "mfma", "kernel": DOMINANT_KERNEL, "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
+                "traffic": traffic,
+                "avg_launch_ms": main_res["step_kernel_ms_avg"],
+                "flop_per_launch": job.flops / main_res["step_launches_per_step"]}
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on a row sample (cpu_baseline)")
+        base = cpu_baseline(job, args.cpu_rows)
+
+    line = {"metric": METRIC, "value": main_res["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded iid N(0,1) Q/K, V per workload recipe; no model weights)",
+            "config": job.config(), "pct_bf16_peak": main_res["pct_bf16_peak"],
+            "roofline": roofline, "cpu_baseline": base,
+            "detail": {args.workload: main_res, **extra},
+            "kernel_source_sha": kernel_source_hash()}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

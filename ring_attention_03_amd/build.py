@@ -24,13 +24,18 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source device flags.  The attention kernel never produces NaNs (its only
+# non-finite value is the -inf of masked scores), so it runs with the IEEE mode
+# bit off: max/min then need no operand canonicalization, which would otherwise
+# double the cost of the row max.
+EXTRA = {"fwd_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile_cmd(src: str) -> tuple[list[str], str]:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", path, "-o", obj]
+        cmd = [HIPCC, *COMMON, *DEVICE, *EXTRA.get(src, []), "-x", "hip", "-c", path, "-o", obj]
     else:  # host-only C++ (validation, planning, launches through the HIP runtime)
         cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
     return cmd, obj

@@ -9,51 +9,89 @@
 // log-sum-exp.  The same kernel run over a whole sequence is full causal
 // prefill.
 //
-// Work decomposition.  A workgroup owns (sequence, row tile, group of query
-// heads that share one key/value head).  Each wave owns 64 query rows of one
-// head and keeps them in registers; the key/value tile (64 keys) is staged in
-// LDS once per workgroup and read by every wave, so a tile is reused by all
-// query heads of its GQA group.
+// Work decomposition.  A workgroup of 8 waves owns (sequence, row tile, group
+// of query heads that share one key/value head); each wave owns 32 query rows
+// of one head, kept in registers.  Key/value tiles of 64 keys are copied from
+// HBM straight into LDS (global_load_lds, no register staging), double
+// buffered, and read by all 8 waves, so a tile is shared by every query head
+// of its GQA group.  A wave needs under 128 VGPRs, so two workgroups - four
+// waves per SIMD - share a CU, and the hardware overlaps one wave's MFMAs with
+// another's softmax arithmetic.  (A single wave cannot issue vector
+// instructions fast enough to keep the VALU busy on its own, which is why the
+// overlap is left to several resident waves rather than to one wave's
+// instruction order.)
 //
 // Register layouts (v_mfma_f32_32x32x16_bf16: A is 32x16, B is 16x32, lane l
 // supplies row/col l%32 and k-slots 8*(l/32)..+7; D lane l holds column l%32,
 // rows 8*(e/4) + 4*(l/32) + e%4 for e = 0..15):
-//  * scores are computed transposed, S^T = K Q^T (A = K from LDS, B = Q from
-//    registers), so a lane holds 16 keys of ONE query: the row max and row sum
-//    are lane-local plus one exchange with lane l^32;
-//  * the output is computed transposed, O^T = V^T P^T.  The B operand is P^T
-//    straight from the score accumulator, which holds keys in the order
-//    8*(e/4) + 4*(l/32) + e%4; V^T is stored in LDS with its keys permuted the
-//    same way so that each lane's A operand is one 16-byte LDS read.
+//  * scores are computed transposed, S^T = K Q^T (A = K rows from LDS, B = Q
+//    from registers), so a lane holds keys of ONE query: the row max and row
+//    sum are lane-local plus one v_permlane32_swap;
+//  * the output is computed transposed, O^T = V^T P^T.  B is P^T taken
+//    straight from the score accumulator; A (V^T) is gathered from row-major
+//    V in LDS by ds_read_b64_tr_b16 (within each 16 lanes, lane j receives
+//    element j%4 of the 4-element row read by lane 4i + j/4, for i = 0..3),
+//    with addresses chosen so the key order matches the accumulator's.
+//
+// The reference max of each row is updated lazily: the exponentials of a block
+// are taken against the current reference unless some score exceeds it by
+// more than 2^8 (p <= 256 keeps fp32 exact in range and bf16 at its usual
+// relative precision); only then - or on a row's first block - is the
+// accumulator rescaled and the reference moved to the row max.  O and LSE are
+// normalised with the same reference, so the result does not depend on which
+// reference was used.
 #include "kernels.h"
 
 namespace attnring {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
 
-constexpr int D = kHeadDim;  // 64
-constexpr int BK = 64;       // keys per LDS tile
-constexpr int QB = 2;        // 32-row query blocks per wave (64 rows)
-constexpr int KSTR = D + 8;  // K row stride in LDS (bf16 elements): 144 B, conflict-free 16-B reads
-constexpr int VSTR = BK + 8; // V^T row stride in LDS
+constexpr int D = kHeadDim;       // 64
+constexpr int NW = 8;             // waves per workgroup
+constexpr int QW = 32;            // query rows per wave
+constexpr int BT = 64;            // keys per LDS tile
+constexpr int BPT = BT / 32;      // 32-key blocks per tile
+static_assert(BPT == 2, "the tile loop handles two blocks per tile");
+constexpr int TILE_ELEMS = BT * D;
+constexpr float RESCALE_LIMIT = 8.0f;  // log2 units: scores may exceed the reference by this much
 
-// Position inside a 16-key group where key j is stored in the V^T tile: the
-// inverse of the accumulator's key order (see the file comment).
-__device__ __forceinline__ int vt_pos(int key) {
-  const int j = key & 15;
-  return (key & ~15) + ((j >> 2) & 1) * 8 + ((j >> 3) & 1) * 4 + (j & 3);
+// LDS tile layout: row-major [key][64], 16-byte chunks XOR-swizzled per row so
+// that the MFMA operand reads hit distinct banks (K: 16-byte reads of 8
+// consecutive rows; V: transposing reads of 4 consecutive rows x 32 bytes).
+__device__ __forceinline__ int k_pos(int key, int chunk) { return chunk ^ (key & 7); }
+__device__ __forceinline__ int v_pos(int key, int chunk) { return chunk ^ ((key & 3) << 1); }
+__device__ __forceinline__ int k_off(int key, int chunk) { return key * D + (k_pos(key, chunk) << 3); }
+__device__ __forceinline__ int v_off(int key, int chunk) { return key * D + (v_pos(key, chunk) << 3); }
+
+template <bool B>
+struct MaskTag {
+  static constexpr bool value = B;
+};
+
+__device__ __forceinline__ float max_halves(float x) {
+  // max of x over lanes l and l^32 (v_permlane32_swap exchanges the wave halves)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
-
-template <int NW, int HPW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BK * KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * VSTR];
+template <int HPW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void fwd_bf16_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned short lds_k[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) unsigned short lds_v[2][TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -67,219 +105,205 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   int s = 0;
   while (unit >= p.unit_off[s + 1]) ++s;
   const int tile = (p.unit_off[s + 1] - 1) - unit;  // heaviest (last) row tile first
-  const int rows_per_tile = QB * 32 * (NW / HPW);
-  const int r0 = tile * rows_per_tile;
+  constexpr int ROWS = QW * (NW / HPW);
+  const int r0 = tile * ROWS;
   const int Lq = p.q_len[s], Lk = p.k_len[s];
   const int qp0 = p.q_pos0[s], kp0 = p.k_pos0[s];
   const int group = p.hq / p.hkv;
   const int head = hg * HPW + (wave % HPW);
   const int kvh = (hg * HPW) / group;
-  const int rw0 = r0 + (wave / HPW) * (QB * 32);  // this wave's first row (within the sequence)
+  const int rw0 = r0 + (wave / HPW) * QW;  // this wave's first row (within the sequence)
 
   // keys [0, kend) can be visible to some row of the tile; keys [0, kfull) to all of them
-  const int last_row = min(r0 + rows_per_tile, Lq) - 1;
+  const int last_row = min(r0 + ROWS, Lq) - 1;
   int kend = Lk, kfull = Lk;
   if (p.causal) {
     kend = min(Lk, max(0, qp0 + last_row - kp0 + 1));
     kfull = min(Lk, max(0, qp0 + r0 - kp0 + 1));
   }
-  const int ntiles = (kend + BK - 1) / BK;
+  const int nblk = (kend + 31) >> 5;
+  const int ntile = (kend + BT - 1) / BT;
 
-  const __bf16* qg = reinterpret_cast<const __bf16*>(p.q);
-  const __bf16* kg = reinterpret_cast<const __bf16*>(p.k) +
-                     ((size_t)p.k_row0[s] * p.hkv + kvh) * D;
-  const __bf16* vg = reinterpret_cast<const __bf16*>(p.v) +
-                     ((size_t)p.k_row0[s] * p.hkv + kvh) * D;
+  // ---- this wave's queries as MFMA B operands: qr[ks] = q[row][16*ks + 8*half .. +7]
+  bf16x8 qr[4];
+  {
+    const int row = rw0 + l32;
+    const __bf16* src = reinterpret_cast<const __bf16*>(p.q) +
+                        ((size_t)(p.q_row0[s] + row) * p.hq + head) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qr[ks] = row < Lq ? *reinterpret_cast<const bf16x8*>(src + ks * 16) : bf16x8{};
+  }
+
+  // ---- tile copy HBM -> LDS: 16-byte slot i of a tile (lane-linear per wave and
+  // instruction) is (key row i/8, position i%8) and holds global chunk
+  // position ^ swizzle(row).  A pass of the workgroup fills NW*64 slots (NW*8
+  // rows, a multiple of 8, so every pass sees the same swizzle); keys past the
+  // end read the last row instead (finite data, masked out of the scores).
+  constexpr int ROWS_PER_PASS = NW * 8;
+  constexpr int PASSES = BT / ROWS_PER_PASS;
+  const int slot_key = tid >> 3, slot_pos = tid & 7;
+  const unsigned short* kg = reinterpret_cast<const unsigned short*>(p.k) +
+                             ((size_t)p.k_row0[s] * p.hkv + kvh) * D +
+                             ((slot_pos ^ (slot_key & 7)) << 3);
+  const unsigned short* vg = reinterpret_cast<const unsigned short*>(p.v) +
+                             ((size_t)p.k_row0[s] * p.hkv + kvh) * D +
+                             ((slot_pos ^ ((slot_key & 3) << 1)) << 3);
   const size_t kstride = (size_t)p.hkv * D;
-
-  // ---- this wave's queries as MFMA B operands: Qr[qb][ks] = q[row][ks*16 + 8*half .. +7]
-  bf16x8 Qr[QB][4];
+  auto copy_tile = [&](int t, int buf) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = rw0 + qb * 32 + l32;
-    const __bf16* src = qg + ((size_t)(p.q_row0[s] + row) * p.hq + head) * D + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (row < Lq) {
-        Qr[qb][ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
-      } else {
-        Qr[qb][ks] = bf16x8{};
-      }
-    }
-  }
-
-  // ---- cooperative tile loads: BK keys x 8 chunks of 8 bf16, for K and for V
-  constexpr int CHUNKS = BK * (D / 8);
-  constexpr int PER_THREAD = (CHUNKS + NW * 64 - 1) / (NW * 64);
-  u16x8 kreg[PER_THREAD], vreg[PER_THREAD];
-
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int c = tid + i * NW * 64;
-      const int kr = c >> 3, ch = c & 7;
-      const int key = t * BK + kr;
-      if (c < CHUNKS && key < Lk) {
-        kreg[i] = *reinterpret_cast<const u16x8*>(kg + key * kstride + ch * 8);
-        vreg[i] = *reinterpret_cast<const u16x8*>(vg + key * kstride + ch * 8);
-      } else {
-        kreg[i] = u16x8{};
-        vreg[i] = u16x8{};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int c = tid + i * NW * 64;
-      if (c < CHUNKS) {
-        const int kr = c >> 3, ch = c & 7;
-        *reinterpret_cast<u16x8*>(reinterpret_cast<unsigned short*>(&Ks[buf][kr * KSTR + ch * 8])) =
-            kreg[i];
-        unsigned short* vt = reinterpret_cast<unsigned short*>(&Vt[buf][0]);
-        const int pos = vt_pos(kr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vt[(ch * 8 + j) * VSTR + pos] = vreg[i][j];
-      }
+    for (int j = 0; j < PASSES; ++j) {
+      const int key = min(t * BT + j * ROWS_PER_PASS + slot_key, Lk - 1);
+      const int dst = j * ROWS_PER_PASS * D + wave * 512;  // this wave's 64 slots of the pass
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(kg + key * kstride),
+                                       (lds_void*)&lds_k[buf][dst], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(vg + key * kstride),
+                                       (lds_void*)&lds_v[buf][dst], 16, 0, 0);
     }
   };
 
-  // ---- running state: O^T accumulators, row max (log2 units) and lane-partial row sums
-  f32x16 acc[2][QB];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) acc[db][qb] = f32x16{};
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-  }
+  // ---- per-lane constants of the operand reads
+  // V (A operand of O^T via transposing reads): lane = 16*g + r
+  const int g16 = (lane >> 4) & 3, r16 = lane & 15;
+  const int v_key = 4 * (g16 >> 1) + (r16 >> 2);             // + 16*step (+8 for the upper 4 slots)
+  const int v_chunk = 2 * (g16 & 1) + ((r16 & 3) >> 1);      // + 4*dblk
+  const int v_sub = 4 * (r16 & 1);                          // element offset inside the chunk
+
+  f32x16 acc[2];  // O^T, [dblk]
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+  float m_run = -INFINITY;  // reference max of this lane's query (log2 units, scaled)
+  float l_run = 0.f;        // lane-partial sum of 2^(s*c - m_run)
   const float c2 = p.scale_log2;
+  f32x16 S;                 // scores of the current block: keys x this wave's 32 queries
+  bf16x8 P[2];              // bf16 probabilities of the current block, per 16-key step
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-
-    // S^T = K Q^T for 64 keys x 64 queries: sc[kb][qb] holds keys kb*32.., queries qb*32..
-    f32x16 sc[2][QB];
+  // exponentials of the block against the current reference max (-> P, lane-partial sum)
+  auto exps = [&](float& rs) {
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = f32x16{};
+      for (int j = 0; j < 8; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(S[st * 8 + j], c2, -m_use));
+        rs += pv;
+        P[st][j] = (__bf16)pv;
+      }
+  };
+
+  // S^T = K Q^T for the 32 keys of block b (rows (b % BPT) * 32.. of LDS buffer buf)
+  auto scores = [&](int b, int buf) {
+    const unsigned short* kt = lds_k[buf];
+    const int row = (b % BPT) * 32 + l32;
+    S = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[k_off(row, 2 * ks + half)]);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ks], S, 0, 0, 0);
+    }
+  };
+  auto mask = [&](int b) {
+    const int qpos = qp0 + rw0 + l32;
+    int last = Lk - 1;
+    if (p.causal) last = min(last, qpos - kp0);
+    const int lim = last - b * 32 - half * 4;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&Ks[buf][(kb * 32 + l32) * KSTR + ks * 16 + half * 8]);
+    for (int e = 0; e < 16; ++e) {
+      const int off = (e >> 2) * 8 + (e & 3);
+      S[e] = off <= lim ? S[e] : -INFINITY;
+    }
+  };
+  // Decide whether the block may use the current reference max: it may unless
+  // some score exceeds the reference by more than 2^8 (kept as a threshold in
+  // raw score units, moved only with the reference) or the row has no
+  // reference yet.  Otherwise raise the reference to the row max and rescale.
+  float thr = -INFINITY;  // raw-score threshold: scores above it need a new reference
+  auto settle_reference = [&]() {
+    float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);  // chains of 3-input max over the lane's 16 keys
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qr[qb][ks], sc[kb][qb], 0, 0, 0);
+    for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, S[e]), S[e + 1]);
+    mx = fmaxf(mx, S[15]);
+    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY || mx > thr) != 0) {  // wave-uniform, rare
+      const float m_new = fmaxf(m_run, max_halves(mx) * c2);
+      if (m_new > m_run) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was -inf
+        l_run *= alpha;
+        acc[0] *= alpha;
+        acc[1] *= alpha;
+        m_run = m_new;
+        thr = (m_new + RESCALE_LIMIT) / c2;
       }
     }
+  };
 
-    // mask: only tiles that reach past the keys every row can see.  Key
-    // kb*32 + 8*(e/4) + 4*half + e%4 of the tile is visible to this lane's
-    // query iff it is <= lim; written as selects (no divergent branches).
-    const int k0 = t * BK;
-    if (k0 + BK > kfull) {
+  // one 32-key block b (keys 32b.. of the sequence chunk) from LDS buffer buf
+  auto block = [&](auto masked_tag, int b, int buf) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    scores(b, buf);
+    if constexpr (MASKED) mask(b);
+    settle_reference();
+    float rs;
+    exps(rs);
+    l_run += rs;
+    // O^T += V^T P^T over two 16-key steps
+    const lds_u16* vt = (const lds_u16*)(const unsigned short*)lds_v[buf];
+    const int kbase = (b % BPT) * 32;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qpos = qp0 + rw0 + qb * 32 + l32;
-        int last = Lk - 1;                                 // last key index of the sequence
-        if (p.causal) last = min(last, qpos - kp0);        // ... and not in the query's future
-        const int lim = last - k0 - half * 4;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int off = kb * 32 + (e >> 2) * 8 + (e & 3);
-            sc[kb][qb][e] = off <= lim ? sc[kb][qb][e] : -INFINITY;
-          }
-      }
-    }
-
-    // online softmax in base 2
-    bf16x8 pb[2][QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][qb][e]);
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run[qb], mx * c2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-      m_run[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][hh * 8 + j], c2, -m_use));
-            rs += pv;
-            pb[kb][qb][hh][j] = (__bf16)pv;
-          }
-      l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) acc[db][qb] *= alpha;
-    }
-
-    // O^T += V^T P^T over 4 steps of 16 keys
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kb = st >> 1, hh = st & 1;
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&Vt[buf][(db * 32 + l32) * VSTR + st * 16 + half * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][qb][hh], acc[db][qb], 0, 0, 0);
+        const int key_lo = kbase + st * 16 + v_key;
+        const int c = 4 * db + v_chunk;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + v_off(key_lo, c) + v_sub));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + v_off(key_lo + 8, c) + v_sub));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[st], acc[db], 0, 0, 0);
       }
     }
+  };
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+  // blocks [0, nfull) are visible to every row of the tile; later ones need the mask
+  const int nfull = min(nblk, kfull >> 5);
+  if (ntile > 0) copy_tile(0, 0);
+  for (int t = 0; t < ntile; ++t) {
+    // tile t has landed in buffer t&1 (own copies waited for, then the barrier);
+    // every wave is done with tile t-1, so its buffer takes tile t+1
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     __syncthreads();
+    if (t + 1 < ntile) copy_tile(t + 1, (t + 1) & 1);
+    const int b0 = t * BPT;
+    if (b0 + 1 < nfull) {
+      block(MaskTag<false>{}, b0, t & 1);
+      block(MaskTag<false>{}, b0 + 1, t & 1);
+    } else {
+      if (b0 < nfull) block(MaskTag<false>{}, b0, t & 1);
+      else block(MaskTag<true>{}, b0, t & 1);
+      if (b0 + 1 < nblk) block(MaskTag<true>{}, b0 + 1, t & 1);
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
-  float* og = p.o;
+  const float l_tot = sum_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int row = rw0 + l32;
+  if (row < Lq) {
+    const size_t grow = (size_t)(p.q_row0[s] + row);
+    float* dst = p.o + (grow * p.hq + head) * D + half * 4;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + xor32(l_run[qb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int row = rw0 + qb * 32 + l32;
-    if (row < Lq) {
-      const size_t grow = (size_t)(p.q_row0[s] + row);
-      float* dst = og + (grow * p.hq + head) * D + half * 4;
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 v4;
-          v4[0] = acc[db][qb][i * 4 + 0] * inv;
-          v4[1] = acc[db][qb][i * 4 + 1] * inv;
-          v4[2] = acc[db][qb][i * 4 + 2] * inv;
-          v4[3] = acc[db][qb][i * 4 + 3] * inv;
-          *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = v4;
-        }
-      if (half == 0) {
-        const float lse = l_tot > 0.f ? (m_run[qb] + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-        p.lse[(size_t)head * p.total_q + grow] = lse;
+      for (int i = 0; i < 4; ++i) {
+        f32x4 v4;
+        v4[0] = acc[db][i * 4 + 0] * inv;
+        v4[1] = acc[db][i * 4 + 1] * inv;
+        v4[2] = acc[db][i * 4 + 2] * inv;
+        v4[3] = acc[db][i * 4 + 3] * inv;
+        *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = v4;
       }
+    if (half == 0) {
+      const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+      p.lse[(size_t)head * p.total_q + grow] = lse;
     }
   }
 }
@@ -289,8 +313,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 Bf16Geometry bf16_geometry(int hq, int hkv) {
   const int group = hq / hkv;
   Bf16Geometry g;
-  g.waves = 8;
-  g.rows_per_wave = QB * 32;
+  g.waves = NW;
+  g.rows_per_wave = QW;
   // heads per workgroup: largest of 8, 4, 2, 1 dividing the GQA group size
   g.heads_per_group = (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
   return g;
@@ -300,10 +324,10 @@ hipError_t launch_fwd_bf16(const FwdParams& p, const Bf16Geometry& geo, int n_un
                            hipStream_t stream) {
   const dim3 grid(n_units * p.n_head_groups), block(geo.waves * 64);
   switch (geo.heads_per_group) {
-    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<8, 8>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((fwd_bf16_kernel<8, 4>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<8, 2>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((fwd_bf16_kernel<8, 1>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<8>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((fwd_bf16_kernel<4>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<2>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<1>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }

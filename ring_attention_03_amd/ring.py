@@ -96,8 +96,16 @@ class RingAttention:
         self.rank = rank
         self.scale = scale
 
-    def run(self, q_local, kv_chunks, o_acc, lse_acc, o_part, lse_part, stream=None) -> int:
+    def run(self, q_local, kv_chunks, o_acc, lse_acc, o_part, lse_part, stream=None,
+            events=None) -> int:
+        """Run the ring; returns the number of steps that launched work.
+
+        ``events``, if a list, receives ``(kind, start, end)`` timing events
+        (kind "step" or "merge") recorded on the launch stream around every
+        launch, for per-kernel timing.
+        """
         lay, r = self.layout, self.rank
+        timed = _EventTimer(events, stream)
         cu = lay.cu
         q_pos0 = lay.pos0(r)
         wrote_state = False
@@ -106,15 +114,19 @@ class RingAttention:
             j = ring_chunk(r, t, lay.n_chunks)
             k_j, v_j = kv_chunks[j]
             dst = (o_part, lse_part) if wrote_state else (o_acc, lse_acc)
-            launched = _native.attn_ring_step(q_local, k_j, v_j, *dst, cu_q=cu, cu_k=cu,
-                                              q_pos0=q_pos0, k_pos0=lay.pos0(j),
-                                              scale=self.scale, causal=True, report_skip=True,
-                                              stream=stream)
+            with timed("step") as mark:
+                launched = _native.attn_ring_step(q_local, k_j, v_j, *dst, cu_q=cu, cu_k=cu,
+                                                  q_pos0=q_pos0, k_pos0=lay.pos0(j),
+                                                  scale=self.scale, causal=True,
+                                                  report_skip=True, stream=stream)
+                mark(launched)
             if not launched:
                 continue
             active += 1
             if wrote_state:
-                _native.attn_ring_merge(o_acc, lse_acc, o_part, lse_part, stream=stream)
+                with timed("merge") as mark:
+                    _native.attn_ring_merge(o_acc, lse_acc, o_part, lse_part, stream=stream)
+                    mark(True)
             wrote_state = True
         if not wrote_state:  # every chunk was in the future: the state is the identity
             k_j, v_j = kv_chunks[ring_chunk(r, 0, lay.n_chunks)]
@@ -122,3 +134,37 @@ class RingAttention:
                                    q_pos0=q_pos0, k_pos0=lay.pos0(r), scale=self.scale,
                                    causal=True, report_skip=False, stream=stream)
         return active
+
+
+class _EventTimer:
+    """Context manager factory recording HIP events around launches (no-op without a list)."""
+
+    def __init__(self, sink, stream):
+        self.sink = sink
+        self.stream = stream
+
+    def __call__(self, kind):
+        return _EventSpan(self, kind)
+
+
+class _EventSpan:
+    def __init__(self, timer, kind):
+        self.timer, self.kind = timer, kind
+        self.keep = False
+        self.start = None
+
+    def __enter__(self):
+        if self.timer.sink is not None:
+            self.start = torch.cuda.Event(enable_timing=True)
+            self.start.record(self.timer.stream)
+        return self._mark
+
+    def _mark(self, launched):
+        self.keep = bool(launched)
+
+    def __exit__(self, *exc):
+        if self.timer.sink is not None and self.keep and exc[0] is None:
+            end = torch.cuda.Event(enable_timing=True)
+            end.record(self.timer.stream)
+            self.timer.sink.append((self.kind, self.start, end))
+        return False
