@@ -36,8 +36,8 @@ KERNEL_SOURCES = ["fwd_bf16.hip", "kernels.h"]
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="ring_64k_rank7")
     ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,varlen_ulysses_rank7",
                     help="comma list of further workloads measured in the same run ('' for none)")

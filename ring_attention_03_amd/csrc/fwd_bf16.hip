@@ -58,9 +58,9 @@ typedef __attribute__((address_space(1))) const void global_cvoid;
 constexpr int D = kHeadDim;       // 64
 constexpr int NW = 8;             // waves per workgroup
 constexpr int QW = 32;            // query rows per wave
-constexpr int BT = 64;            // keys per LDS tile
+constexpr int BT = 128;           // keys per LDS tile
 constexpr int BPT = BT / 32;      // 32-key blocks per tile
-static_assert(BPT == 2, "the tile loop handles two blocks per tile");
+
 constexpr int TILE_ELEMS = BT * D;
 constexpr float RESCALE_LIMIT = 8.0f;  // log2 units: scores may exceed the reference by this much
 
@@ -75,6 +75,10 @@ __device__ __forceinline__ int v_off(int key, int chunk) { return key * D + (v_p
 template <bool B>
 struct MaskTag {
   static constexpr bool value = B;
+};
+template <int V>
+struct Int {
+  static constexpr int value = V;
 };
 
 __device__ __forceinline__ float max_halves(float x) {
@@ -162,12 +166,26 @@ void fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  // ---- per-lane constants of the operand reads
-  // V (A operand of O^T via transposing reads): lane = 16*g + r
-  const int g16 = (lane >> 4) & 3, r16 = lane & 15;
-  const int v_key = 4 * (g16 >> 1) + (r16 >> 2);             // + 16*step (+8 for the upper 4 slots)
-  const int v_chunk = 2 * (g16 & 1) + ((r16 & 3) >> 1);      // + 4*dblk
-  const int v_sub = 4 * (r16 & 1);                          // element offset inside the chunk
+  // ---- per-lane parts of the LDS operand addresses (everything else is an immediate)
+  // K (A operand of S^T): row l32 (+32 per block, +BT per buffer), chunk 2*ks + half;
+  // the swizzle depends on row & 7 = l32 & 7 only.
+  int k_lane[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) k_lane[ks] = k_off(l32, 2 * ks + half) * 2;
+  // V (A operand of O^T via transposing reads): lane = 16*g + r reads key
+  // 16*step + 4*(g/2) + r/4 (+8 for the upper 4 k-slots) at d = 32*dblk +
+  // 16*(g%2) + 4*(r%4); the swizzle depends on key & 3 = (r/4) & 3 only.
+  int v_lane[2];
+  {
+    const int g16 = (lane >> 4) & 3, r16 = lane & 15;
+    const int v_key = 4 * (g16 >> 1) + (r16 >> 2);
+    const int v_chunk = 2 * (g16 & 1) + ((r16 & 3) >> 1);
+    const int v_sub = 4 * (r16 & 1);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) v_lane[db] = (v_off(v_key, 4 * db + v_chunk) + v_sub) * 2;
+  }
+  const lds_u16* lds_k0 = (const lds_u16*)(const unsigned short*)lds_k;
+  const lds_u16* lds_v0 = (const lds_u16*)(const unsigned short*)lds_v;
 
   f32x16 acc[2];  // O^T, [dblk]
   acc[0] = f32x16{};
@@ -178,28 +196,31 @@ void fwd_bf16_kernel(FwdParams p) {
   f32x16 S;                 // scores of the current block: keys x this wave's 32 queries
   bf16x8 P[2];              // bf16 probabilities of the current block, per 16-key step
 
-  // exponentials of the block against the current reference max (-> P, lane-partial sum)
+  // exponentials of the block against the current reference max (-> P, lane-partial sum;
+  // four partial sums keep the additions independent)
   auto exps = [&](float& rs) {
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    rs = 0.f;
+    float part[4];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(S[st * 8 + j], c2, -m_use));
-        rs += pv;
+        const int k = (st * 8 + j) & 3;
+        part[k] = (st == 0 && j < 4) ? pv : part[k] + pv;
         P[st][j] = (__bf16)pv;
       }
+    rs = (part[0] + part[1]) + (part[2] + part[3]);
   };
 
-  // S^T = K Q^T for the 32 keys of block b (rows (b % BPT) * 32.. of LDS buffer buf)
-  auto scores = [&](int b, int buf) {
-    const unsigned short* kt = lds_k[buf];
-    const int row = (b % BPT) * 32 + l32;
+  // S^T = K Q^T for the 32 keys at row offset `row0` of LDS buffer `buf` (compile-time)
+  auto scores = [&](auto buf_tag, auto half_tag) {
+    constexpr int BASE = (decltype(buf_tag)::value * TILE_ELEMS + decltype(half_tag)::value * 32 * D) * 2;
     S = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[k_off(row, 2 * ks + half)]);
+      const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
+          (const __attribute__((address_space(3))) char*)lds_k0 + k_lane[ks] + BASE);
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ks], S, 0, 0, 0);
     }
   };
@@ -224,7 +245,7 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, S[e]), S[e + 1]);
     mx = fmaxf(mx, S[15]);
-    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY || mx > thr) != 0) {  // wave-uniform, rare
+    if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {  // wave-uniform, rare (thr = -inf before the first block)
       const float m_new = fmaxf(m_run, max_halves(mx) * c2);
       if (m_new > m_run) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was -inf
@@ -237,26 +258,25 @@ void fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  // one 32-key block b (keys 32b.. of the sequence chunk) from LDS buffer buf
-  auto block = [&](auto masked_tag, int b, int buf) {
+  // one 32-key block b (keys 32b.. of the sequence chunk): the (b%2)-th half of LDS buffer buf
+  auto block = [&](auto masked_tag, auto buf_tag, auto half_tag, int b) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    scores(b, buf);
+    scores(buf_tag, half_tag);
     if constexpr (MASKED) mask(b);
     settle_reference();
     float rs;
     exps(rs);
     l_run += rs;
     // O^T += V^T P^T over two 16-key steps
-    const lds_u16* vt = (const lds_u16*)(const unsigned short*)lds_v[buf];
-    const int kbase = (b % BPT) * 32;
+    constexpr int VBASE = (decltype(buf_tag)::value * TILE_ELEMS + decltype(half_tag)::value * 32 * D) * 2;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const int key_lo = kbase + st * 16 + v_key;
-        const int c = 4 * db + v_chunk;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + v_off(key_lo, c) + v_sub));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + v_off(key_lo + 8, c) + v_sub));
+        const __attribute__((address_space(3))) char* vb =
+            (const __attribute__((address_space(3))) char*)lds_v0 + v_lane[db] + VBASE + st * 16 * D * 2;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * D * 2));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[st], acc[db], 0, 0, 0);
       }
@@ -265,22 +285,30 @@ void fwd_bf16_kernel(FwdParams p) {
 
   // blocks [0, nfull) are visible to every row of the tile; later ones need the mask
   const int nfull = min(nblk, kfull >> 5);
-  if (ntile > 0) copy_tile(0, 0);
-  for (int t = 0; t < ntile; ++t) {
-    // tile t has landed in buffer t&1 (own copies waited for, then the barrier);
-    // every wave is done with tile t-1, so its buffer takes tile t+1
+  // one tile: it has landed in buffer BUF (own copies waited for, then the
+  // barrier); every wave is done with the other buffer, which takes tile t+1
+  auto tile_step = [&](auto buf_tag, int t) {
+    constexpr int BUF = decltype(buf_tag)::value;
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     __syncthreads();
-    if (t + 1 < ntile) copy_tile(t + 1, (t + 1) & 1);
+    if (t + 1 < ntile) copy_tile(t + 1, BUF ^ 1);
     const int b0 = t * BPT;
-    if (b0 + 1 < nfull) {
-      block(MaskTag<false>{}, b0, t & 1);
-      block(MaskTag<false>{}, b0 + 1, t & 1);
+    if (b0 + 3 < nfull) {
+      block(MaskTag<false>{}, buf_tag, Int<0>{}, b0);
+      block(MaskTag<false>{}, buf_tag, Int<1>{}, b0 + 1);
+      block(MaskTag<false>{}, buf_tag, Int<2>{}, b0 + 2);
+      block(MaskTag<false>{}, buf_tag, Int<3>{}, b0 + 3);
     } else {
-      if (b0 < nfull) block(MaskTag<false>{}, b0, t & 1);
-      else block(MaskTag<true>{}, b0, t & 1);
-      if (b0 + 1 < nblk) block(MaskTag<true>{}, b0 + 1, t & 1);
+      if (b0 < nfull) block(MaskTag<false>{}, buf_tag, Int<0>{}, b0); else block(MaskTag<true>{}, buf_tag, Int<0>{}, b0);
+      if (b0 + 1 < nfull) block(MaskTag<false>{}, buf_tag, Int<1>{}, b0 + 1); else if (b0 + 1 < nblk) block(MaskTag<true>{}, buf_tag, Int<1>{}, b0 + 1);
+      if (b0 + 2 < nfull) block(MaskTag<false>{}, buf_tag, Int<2>{}, b0 + 2); else if (b0 + 2 < nblk) block(MaskTag<true>{}, buf_tag, Int<2>{}, b0 + 2);
+      if (b0 + 3 < nblk) block(MaskTag<true>{}, buf_tag, Int<3>{}, b0 + 3);
     }
+  };
+  if (ntile > 0) copy_tile(0, 0);
+  for (int t = 0; t < ntile; t += 2) {
+    tile_step(Int<0>{}, t);
+    if (t + 1 < ntile) tile_step(Int<1>{}, t + 1);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
