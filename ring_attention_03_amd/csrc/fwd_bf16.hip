@@ -62,7 +62,7 @@ constexpr int BT = 128;           // keys per LDS tile
 constexpr int BPT = BT / 32;      // 32-key blocks per tile
 
 constexpr int TILE_ELEMS = BT * D;
-constexpr float RESCALE_LIMIT = 8.0f;  // log2 units: scores may exceed the reference by this much
+constexpr float SUM_LIMIT = 256.0f;  // a block's exponentials are kept when each lane-partial sum is <= 2^8
 
 // LDS tile layout: row-major [key][64], 16-byte chunks XOR-swizzled per row so
 // that the MFMA operand reads hit distinct banks (K: 16-byte reads of 8
@@ -199,7 +199,10 @@ void fwd_bf16_kernel(FwdParams p) {
   // exponentials of the block against the current reference max (-> P, lane-partial sum;
   // four partial sums keep the additions independent)
   auto exps = [&](float& rs) {
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // Without a reference yet (-inf), use -3e38: every visible score then
+    // overflows to +inf, which sends the block down the exact path, while a
+    // fully masked row still contributes exact zeros.
+    const float m_use = m_run == -INFINITY ? -3.0e38f : m_run;
     float part[4];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -235,39 +238,45 @@ void fwd_bf16_kernel(FwdParams p) {
       S[e] = off <= lim ? S[e] : -INFINITY;
     }
   };
-  // Decide whether the block may use the current reference max: it may unless
-  // some score exceeds the reference by more than 2^8 (kept as a threshold in
-  // raw score units, moved only with the reference) or the row has no
-  // reference yet.  Otherwise raise the reference to the row max and rescale.
-  float thr = -INFINITY;  // raw-score threshold: scores above it need a new reference
+  // raise the reference max of each row to the row max of S (rescaling acc and l)
   auto settle_reference = [&]() {
     float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);  // chains of 3-input max over the lane's 16 keys
 #pragma unroll
     for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, S[e]), S[e + 1]);
     mx = fmaxf(mx, S[15]);
-    if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {  // wave-uniform, rare (thr = -inf before the first block)
-      const float m_new = fmaxf(m_run, max_halves(mx) * c2);
-      if (m_new > m_run) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was -inf
-        l_run *= alpha;
-        acc[0] *= alpha;
-        acc[1] *= alpha;
-        m_run = m_new;
-        thr = (m_new + RESCALE_LIMIT) / c2;
-      }
+    const float m_new = fmaxf(m_run, max_halves(mx) * c2);
+    if (m_new > m_run) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was -inf
+      l_run *= alpha;
+      acc[0] *= alpha;
+      acc[1] *= alpha;
+      m_run = m_new;
     }
   };
 
-  // one 32-key block b (keys 32b.. of the sequence chunk): the (b%2)-th half of LDS buffer buf
-  auto block = [&](auto masked_tag, auto buf_tag, auto half_tag, int b) {
+  // softmax of the scores of block b (keys 32b.. of the sequence chunk) -> P, l.
+  // Fast path: exponentials against the current reference max, kept when every
+  // lane-partial row sum is <= 2^8 (then no score exceeded the reference by more
+  // than 8 in log2 units, so p <= 256).  Otherwise - the row's first visible
+  // block (reference -inf, sums inf), or a score that outgrew the reference -
+  // the scores are recomputed (they are not kept live: registers), the
+  // reference is raised to the row max with acc and l rescaled, and the
+  // exponentials redone.
+  auto softmax = [&](auto masked_tag, auto buf_tag, auto half_tag, int b) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    scores(buf_tag, half_tag);
     if constexpr (MASKED) mask(b);
-    settle_reference();
     float rs;
     exps(rs);
+    if (__builtin_amdgcn_ballot_w64(rs > SUM_LIMIT) != 0) {  // wave-uniform, rare
+      scores(buf_tag, half_tag);
+      if constexpr (MASKED) mask(b);
+      settle_reference();
+      exps(rs);
+    }
     l_run += rs;
-    // O^T += V^T P^T over two 16-key steps
+  };
+  // O^T += V^T P^T for the block in quarter `half_tag` of LDS buffer `buf_tag`
+  auto pv = [&](auto buf_tag, auto half_tag) {
     constexpr int VBASE = (decltype(buf_tag)::value * TILE_ELEMS + decltype(half_tag)::value * 32 * D) * 2;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -282,6 +291,16 @@ void fwd_bf16_kernel(FwdParams p) {
       }
     }
   };
+  // One block of a tile.  Once the exponentials of block b have consumed the
+  // scores, the scores of the tile's next block are issued into the same
+  // registers BEFORE O += P V of block b, so the matrix core finishes them
+  // first and the next softmax overlaps the P V products.
+  auto block = [&](auto masked_tag, auto buf_tag, auto half_tag, int b) {
+    softmax(masked_tag, buf_tag, half_tag, b);
+    constexpr int H = decltype(half_tag)::value;
+    if constexpr (H + 1 < BPT) scores(buf_tag, Int<H + 1>{});
+    pv(buf_tag, half_tag);
+  };
 
   // blocks [0, nfull) are visible to every row of the tile; later ones need the mask
   const int nfull = min(nblk, kfull >> 5);
@@ -293,6 +312,7 @@ void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
     if (t + 1 < ntile) copy_tile(t + 1, BUF ^ 1);
     const int b0 = t * BPT;
+    scores(buf_tag, Int<0>{});
     if (b0 + 3 < nfull) {
       block(MaskTag<false>{}, buf_tag, Int<0>{}, b0);
       block(MaskTag<false>{}, buf_tag, Int<1>{}, b0 + 1);

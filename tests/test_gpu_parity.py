@@ -165,6 +165,23 @@ def test_uniform_v_and_large_scores():
     assert_close(o, lse, o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, "scores x30, uniform V")
 
 
+def test_very_negative_scores_keep_their_softmax():
+    # Every score is about -1000 (log2 units): exponentials against any fixed
+    # reference underflow, so the kernel must take each row's true maximum.
+    g = torch.Generator().manual_seed(21)
+    t = 600
+    u = torch.randn(64, generator=g)
+    u = u / u.norm()
+    k = (u + 0.02 * torch.randn(t, 1, 64, generator=g))  # every key close to u
+    q = -(1000.0 * 8.0 / 1.4427) * u + 0.5 * torch.randn(t, 8, 64, generator=g)
+    v = torch.randn(t, 1, 64, generator=g)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    o, lse = _prefill(q, k, v)
+    o_ref, lse_ref = causal_attention_ref(q, k, v)
+    assert float(lse_ref.max()) < -400  # the scores really are that negative
+    assert_close(o, lse, o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, "very negative scores")
+
+
 def test_fully_masked_step_skips_or_writes_identity():
     g = torch.Generator().manual_seed(16)
     q = torch.randn(100, 8, 64, generator=g).to(torch.bfloat16).cuda()
