@@ -10,7 +10,7 @@ Prints ONE JSON line.  ``value`` is algorithmic TFLOP/s: 4 * head_dim * Hq
 flops per causal (query, key) pair (2*d for the score, 2*d for the weighted
 sum of values); masked work and softmax arithmetic are not counted.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload ring_64k_rank7]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--workload ring_64k_rank7]
 """
 
 from __future__ import annotations
@@ -43,10 +43,14 @@ def parse_args():
                     help="comma list of further workloads measured in the same run ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=384,
+    ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows of the oracle sample (all heads, all ring steps)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (for counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only derive HBM bytes per attention launch from four rocprofv3 --pmc output "
+                         "folders (FETCH_SIZE and WRITE_SIZE of a bench run, then of --calibrate-copy) "
+                         "and write them to " + os.path.relpath(TRAFFIC_FILE, ROOT))
     return ap.parse_args()
 
 
@@ -209,7 +213,11 @@ def cpu_baseline(job, nrows):
                       f"{flops / 1e9:.1f} GFLOP algorithmic; host {cpu}, os.cpu_count()={os.cpu_count()}"}
 
 
+COPY_KERNEL = "neg_kernel"  # torch's elementwise negation: reads n words, writes n words
+
+
 def calibrate_copy(mib):
+    """A plain streaming kernel of known size (y = -x over `mib` MiB) for counter scaling."""
     import torch
 
     n = mib * (1 << 20) // 4
@@ -217,16 +225,66 @@ def calibrate_copy(mib):
     y = torch.empty_like(x)
     torch.cuda.synchronize()
     for _ in range(3):
-        y.copy_(x)
+        torch.neg(x, out=y)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 3}), flush=True)
 
 
+def _counter_per_dispatch(folder, counter, name_part):
+    """Mean over matching dispatches of one counter (summed over its instances) in a --pmc run."""
+    import csv
+    import glob
+
+    per_dispatch = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    for path in files:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    key = (path, r["Dispatch_Id"])
+                    per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    if not per_dispatch:
+        raise SystemExit(f"no {counter} values for kernels matching {name_part!r} under {folder}")
+    vals = list(per_dispatch.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload, copy_mib):
+    """HBM bytes per attention launch, each counter scaled by its reading for a copy of known size.
+
+    FETCH_SIZE and WRITE_SIZE count KiB moved between L2 and memory per
+    dispatch.  The copy kernel moves exactly copy_mib MiB each way, so
+    factor = bytes moved / (counter * 1024) corrects the counter's unit and
+    coverage.  The result is averaged over all attention launches of the run,
+    like the event-timed launch duration it sits beside.
+    """
+    copy_bytes = copy_mib * (1 << 20)
+    cf, _ = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", COPY_KERNEL)
+    cw, _ = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", COPY_KERNEL)
+    f_kib, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", DOMINANT_KERNEL)
+    w_kib, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", DOMINANT_KERNEL)
+    ff, wf = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    rec = {"kernel": DOMINANT_KERNEL, "kernel_source_sha": kernel_source_hash(), "workload": workload,
+           "bytes_per_launch": f_kib * 1024 * ff + w_kib * 1024 * wf,
+           "fetch_bytes_per_launch": f_kib * 1024 * ff, "write_bytes_per_launch": w_kib * 1024 * wf,
+           "fetch_kib_raw": f_kib, "write_kib_raw": w_kib, "launches": [nf, nw],
+           "copy_mib": copy_mib, "fetch_factor": ff, "write_factor": wf}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, workload=args.workload, copy_mib=args.calibrate_copy or 2048)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
-              "(the ring across GPUs is not part of this build)", file=sys.stderr)
+              "(this library runs one device's share of the ring; it has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
 
