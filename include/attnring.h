@@ -64,7 +64,8 @@ typedef enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_FP32 = 1 } attn_dtype;
 typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = 1,       /* an argument is invalid; nothing enqueued */
-  ATTN_EUNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim != 64); nothing enqueued */
+  ATTN_EUNSUPPORTED = 2, /* valid but not implemented (head_dim != 64, or with bf16 one
+                            sequence's k or v spanning 2 GiB or more); nothing enqueued */
   ATTN_EHIP = 3          /* the HIP launch failed */
 } attn_status;
 

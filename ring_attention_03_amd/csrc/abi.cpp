@@ -106,6 +106,10 @@ attn_status plan_forward(const attn_problem* pr, attn_dtype dt, const void* q, c
 
   const size_t esz = dt == ATTN_DTYPE_BF16 ? 2 : 4;
   const int64_t d = pr->head_dim;
+  // the bf16 kernel addresses one sequence's keys and values with 32-bit byte offsets
+  for (int b = 0; b < nseq && dt == ATTN_DTYPE_BF16; ++b)
+    if ((int64_t)(ck[b + 1] - ck[b]) * pr->num_kv_heads * d * 2 >= (int64_t(1) << 31))
+      return fail(ATTN_EUNSUPPORTED, "sequence %d: keys and values span 2 GiB or more per tensor", b);
   const size_t q_bytes = (size_t)pr->total_q * pr->num_q_heads * d * esz;
   const size_t kv_bytes = (size_t)pr->total_k * pr->num_kv_heads * d * esz;
   const size_t o_bytes = (size_t)pr->total_q * pr->num_q_heads * d * 4;

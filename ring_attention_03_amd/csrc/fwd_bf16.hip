@@ -11,15 +11,20 @@
 //
 // Work decomposition.  A workgroup of 8 waves owns (sequence, row tile, group
 // of query heads that share one key/value head); each wave owns 32 query rows
-// of one head, kept in registers.  Key/value tiles of 64 keys are copied from
-// HBM straight into LDS (global_load_lds, no register staging), double
-// buffered, and read by all 8 waves, so a tile is shared by every query head
-// of its GQA group.  A wave needs under 128 VGPRs, so two workgroups - four
-// waves per SIMD - share a CU, and the hardware overlaps one wave's MFMAs with
-// another's softmax arithmetic.  (A single wave cannot issue vector
-// instructions fast enough to keep the VALU busy on its own, which is why the
-// overlap is left to several resident waves rather than to one wave's
-// instruction order.)
+// of one head, kept in registers.  Key/value tiles of 128 keys are copied from
+// HBM straight into LDS (global_load_lds, no register staging) and read by all
+// 8 waves, so a tile is shared by every query head of its GQA group.  A wave
+// needs at most 128 VGPRs, so two workgroups - four waves per SIMD - share a
+// CU.
+//
+// Software pipeline.  Each wave walks its key range in 32-key blocks; the
+// softmax of block i (vector ALU) is interleaved with O += P V of block i-1
+// and S = K Q^T of block i+1 (matrix cores), which do not depend on it, so a
+// single wave keeps both units busy and the other resident waves fill the
+// gaps.  Keys of block i are read from LDS one step before its softmax and
+// values one step after, so values live one tile longer than keys: LDS holds
+// two key buffers and three value buffers (80 KiB), and one barrier per tile
+// separates the copy of tile t+2 from the last reads of the buffers it reuses.
 //
 // Register layouts (v_mfma_f32_32x32x16_bf16: A is 32x16, B is 16x32, lane l
 // supplies row/col l%32 and k-slots 8*(l/32)..+7; D lane l holds column l%32,
@@ -61,7 +66,10 @@ constexpr int QW = 32;            // query rows per wave
 constexpr int BT = 128;           // keys per LDS tile
 constexpr int BPT = BT / 32;      // 32-key blocks per tile
 
+constexpr int NKB = 2;            // key tile buffers in LDS
+constexpr int NVB = 3;            // value tile buffers in LDS (values are read one tile later)
 constexpr int TILE_ELEMS = BT * D;
+constexpr int TILE_BYTES = TILE_ELEMS * 2;
 constexpr float SUM_LIMIT = 256.0f;  // a block's exponentials are kept when each lane-partial sum is <= 2^8
 
 // LDS tile layout: row-major [key][64], 16-byte chunks XOR-swizzled per row so
@@ -81,6 +89,32 @@ struct Int {
   static constexpr int value = V;
 };
 
+// One 16-byte slot per lane from global memory straight into LDS, lane-linear
+// from the wave-uniform LDS byte address `lds_addr`.  Written as assembly so
+// the compiler does not treat every later LDS read as dependent on it (it would
+// wait for the copy to land before the next ds_read, which defeats the double
+// buffering); the kernel waits for its copies itself, with vmcnt(0) before the
+// barrier that publishes a tile.  M0 carries the LDS address and is restored.
+__device__ __forceinline__ void lds_dma16(const void* gbase, unsigned voff, unsigned lds_addr) {
+  // gbase and lds_addr are wave-uniform; readfirstlane puts them in scalar registers
+  // (readfirstlane returns int: each half goes through unsigned so the low half
+  // is not sign-extended into the high one)
+  const unsigned long long a = (unsigned long long)gbase;
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
+  const void* sbase = (const void*)(((unsigned long long)hi << 32) | (unsigned long long)lo);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+
 __device__ __forceinline__ float max_halves(float x) {
   // max of x over lanes l and l^32 (v_permlane32_swap exchanges the wave halves)
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -94,18 +128,23 @@ __device__ __forceinline__ float sum_halves(float x) {
 template <int HPW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void fwd_bf16_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned short lds_k[2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) unsigned short lds_v[2][TILE_ELEMS];
+  // LDS: NKB key tile buffers, then NVB value tile buffers (16 KiB each)
+  __shared__ __attribute__((aligned(16))) unsigned short lds[(NKB + NVB) * TILE_ELEMS];
 
-  const int tid = threadIdx.x;
+  // (the index builtins directly: the device-library wrappers are compiled with
+  // IEEE mode on and would not inline into this kernel)
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int wg = __builtin_amdgcn_workgroup_id_x();
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
   // ---- which (sequence, row tile, head group) this workgroup owns
-  const int hg = blockIdx.x % p.n_head_groups;
-  const int unit = blockIdx.x / p.n_head_groups;
+  // (the division runs on the vector unit; readfirstlane keeps everything derived
+  // from it in scalar registers)
+  const int unit = __builtin_amdgcn_readfirstlane(wg / p.n_head_groups);
+  const int hg = wg - unit * p.n_head_groups;
   int s = 0;
   while (unit >= p.unit_off[s + 1]) ++s;
   const int tile = (p.unit_off[s + 1] - 1) - unit;  // heaviest (last) row tile first
@@ -115,7 +154,7 @@ void fwd_bf16_kernel(FwdParams p) {
   const int qp0 = p.q_pos0[s], kp0 = p.k_pos0[s];
   const int group = p.hq / p.hkv;
   const int head = hg * HPW + (wave % HPW);
-  const int kvh = (hg * HPW) / group;
+  const int kvh = __builtin_amdgcn_readfirstlane((hg * HPW) / group);
   const int rw0 = r0 + (wave / HPW) * QW;  // this wave's first row (within the sequence)
 
   // keys [0, kend) can be visible to some row of the tile; keys [0, kfull) to all of them
@@ -127,6 +166,8 @@ void fwd_bf16_kernel(FwdParams p) {
   }
   const int nblk = (kend + 31) >> 5;
   const int ntile = (kend + BT - 1) / BT;
+  // blocks [0, nfull) are visible to every row of the tile; later ones need the mask
+  const int nfull = min(nblk, kfull >> 5);
 
   // ---- this wave's queries as MFMA B operands: qr[ks] = q[row][16*ks + 8*half .. +7]
   bf16x8 qr[4];
@@ -147,87 +188,95 @@ void fwd_bf16_kernel(FwdParams p) {
   constexpr int ROWS_PER_PASS = NW * 8;
   constexpr int PASSES = BT / ROWS_PER_PASS;
   const int slot_key = tid >> 3, slot_pos = tid & 7;
-  const unsigned short* kg = reinterpret_cast<const unsigned short*>(p.k) +
-                             ((size_t)p.k_row0[s] * p.hkv + kvh) * D +
-                             ((slot_pos ^ (slot_key & 7)) << 3);
-  const unsigned short* vg = reinterpret_cast<const unsigned short*>(p.v) +
-                             ((size_t)p.k_row0[s] * p.hkv + kvh) * D +
-                             ((slot_pos ^ ((slot_key & 3) << 1)) << 3);
-  const size_t kstride = (size_t)p.hkv * D;
-  auto copy_tile = [&](int t, int buf) {
+  const int kstride = p.hkv * D;  // elements between consecutive keys
+  const size_t kv_base = ((size_t)p.k_row0[s] * p.hkv + kvh) * D;
+  const char* kgb = reinterpret_cast<const char*>(reinterpret_cast<const unsigned short*>(p.k) + kv_base);
+  const char* vgb = reinterpret_cast<const char*>(reinterpret_cast<const unsigned short*>(p.v) + kv_base);
+  // Per-lane byte offsets stay 32-bit (the host bounds a sequence's K/V to 2 GiB),
+  // so the copies use a scalar base plus one vector offset.
+  const unsigned k_lane_off = (slot_pos ^ (slot_key & 7)) << 4;         // bytes within a key row
+  const unsigned v_lane_off = (slot_pos ^ ((slot_key & 3) << 1)) << 4;
+  const unsigned lds_wave = (unsigned)(uintptr_t)(const lds_u16*)(const unsigned short*)lds + wave * 1024;
+  auto copy_tile = [&](int t) __attribute__((always_inline)) {
+    const unsigned kb = (t % NKB) * TILE_BYTES, vb = (NKB + t % NVB) * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < PASSES; ++j) {
       const int key = min(t * BT + j * ROWS_PER_PASS + slot_key, Lk - 1);
-      const int dst = j * ROWS_PER_PASS * D + wave * 512;  // this wave's 64 slots of the pass
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(kg + key * kstride),
-                                       (lds_void*)&lds_k[buf][dst], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(vg + key * kstride),
-                                       (lds_void*)&lds_v[buf][dst], 16, 0, 0);
+      const unsigned row_off = (unsigned)(key * kstride) * 2u;
+      const unsigned dst = lds_wave + j * ROWS_PER_PASS * D * 2;  // this wave's 64 slots of the pass
+      lds_dma16(kgb, row_off + k_lane_off, dst + kb);
+      lds_dma16(vgb, row_off + v_lane_off, dst + vb);
     }
   };
 
-  // ---- per-lane parts of the LDS operand addresses (everything else is an immediate)
-  // K (A operand of S^T): row l32 (+32 per block, +BT per buffer), chunk 2*ks + half;
-  // the swizzle depends on row & 7 = l32 & 7 only.
-  int k_lane[4];
+  // ---- per-lane LDS operand addresses (bytes; the block within a tile is an immediate).
+  // K (A operand of S^T): row l32 (+32 per block), chunk 2*ks + half; the
+  // swizzle depends on row & 7 = l32 & 7 only.  k_addr points into the buffer of
+  // the tile whose keys are read next.
+  int k_addr[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) k_lane[ks] = k_off(l32, 2 * ks + half) * 2;
+  for (int ks = 0; ks < 4; ++ks) k_addr[ks] = k_off(l32, 2 * ks + half) * 2;
   // V (A operand of O^T via transposing reads): lane = 16*g + r reads key
   // 16*step + 4*(g/2) + r/4 (+8 for the upper 4 k-slots) at d = 32*dblk +
   // 16*(g%2) + 4*(r%4); the swizzle depends on key & 3 = (r/4) & 3 only.
-  int v_lane[2];
+  int v_addr[2];
   {
     const int g16 = (lane >> 4) & 3, r16 = lane & 15;
     const int v_key = 4 * (g16 >> 1) + (r16 >> 2);
     const int v_chunk = 2 * (g16 & 1) + ((r16 & 3) >> 1);
     const int v_sub = 4 * (r16 & 1);
 #pragma unroll
-    for (int db = 0; db < 2; ++db) v_lane[db] = (v_off(v_key, 4 * db + v_chunk) + v_sub) * 2;
+    for (int db = 0; db < 2; ++db)
+      v_addr[db] = (NKB * TILE_ELEMS + v_off(v_key, 4 * db + v_chunk) + v_sub) * 2;
   }
-  const lds_u16* lds_k0 = (const lds_u16*)(const unsigned short*)lds_k;
-  const lds_u16* lds_v0 = (const lds_u16*)(const unsigned short*)lds_v;
+  const __attribute__((address_space(3))) char* lds_b =
+      (const __attribute__((address_space(3))) char*)(const lds_u16*)(const unsigned short*)lds;
+  // the values of tile t sit in buffer t % NVB: step v_addr from tile t-1's buffer to tile t's
+  // (v_addr starts at tile 0's)
+  auto advance_v = [&](int t) __attribute__((always_inline)) {
+    const int delta = t == 0 ? 0 : (t % NVB == 0) ? -(NVB - 1) * TILE_BYTES : TILE_BYTES;
+    v_addr[0] += delta;
+    v_addr[1] += delta;
+  };
 
   f32x16 acc[2];  // O^T, [dblk]
   acc[0] = f32x16{};
   acc[1] = f32x16{};
   float m_run = -INFINITY;  // reference max of this lane's query (log2 units, scaled)
+  // Exponent offset.  Without a reference yet it is +3e38: every visible
+  // score then overflows to +inf, which sends the block down the exact path,
+  // while a fully masked row still contributes exact zeros.
+  float neg_m = 3.0e38f;
   float l_run = 0.f;        // lane-partial sum of 2^(s*c - m_run)
   const float c2 = p.scale_log2;
-  f32x16 S;                 // scores of the current block: keys x this wave's 32 queries
-  bf16x8 P[2];              // bf16 probabilities of the current block, per 16-key step
+  f32x16 S[2];              // scores of blocks i (S[i&1]) and i+1: keys x this wave's 32 queries
+  bf16x8 P[2][2];           // bf16 probabilities of blocks i and i-1 ([i&1]), per 16-key step
 
-  // exponentials of the block against the current reference max (-> P, lane-partial sum;
-  // four partial sums keep the additions independent)
-  auto exps = [&](float& rs) {
-    // Without a reference yet (-inf), use -3e38: every visible score then
-    // overflows to +inf, which sends the block down the exact path, while a
-    // fully masked row still contributes exact zeros.
-    const float m_use = m_run == -INFINITY ? -3.0e38f : m_run;
-    float part[4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(S[st * 8 + j], c2, -m_use));
-        const int k = (st * 8 + j) & 3;
-        part[k] = (st == 0 && j < 4) ? pv : part[k] + pv;
-        P[st][j] = (__bf16)pv;
-      }
-    rs = (part[0] + part[1]) + (part[2] + part[3]);
+  // K operand of 16-key step ks of block `sub` in the current key buffer
+  auto kread = [&](int ks, auto sub_tag) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(sub_tag)::value * 32 * D * 2;
+    return *(const __attribute__((address_space(3))) bf16x8*)(lds_b + k_addr[ks] + OFF);
   };
-
-  // S^T = K Q^T for the 32 keys at row offset `row0` of LDS buffer `buf` (compile-time)
-  auto scores = [&](auto buf_tag, auto half_tag) {
-    constexpr int BASE = (decltype(buf_tag)::value * TILE_ELEMS + decltype(half_tag)::value * 32 * D) * 2;
-    S = f32x16{};
+  // V^T operand of (16-key step st, d block db) of block `sub` in the current value buffer
+  auto vread = [&](int st, int db, auto sub_tag) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(sub_tag)::value * 32 * D * 2;
+    const __attribute__((address_space(3))) char* vb = lds_b + v_addr[db] + OFF + st * 16 * D * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * D * 2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // exponentials of the 8 scores of 16-key step st against the current reference
+  // (-> Pst; four independent partial sums)
+  auto exps_half = [&](const f32x16& Sb, bf16x8& Pst, float* part, auto st_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_tag)::value;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
-          (const __attribute__((address_space(3))) char*)lds_k0 + k_lane[ks] + BASE);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ks], S, 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(Sb[ST * 8 + j], c2, neg_m));
+      if (ST == 0 && j < 4) part[j] = pv; else part[j & 3] += pv;
+      Pst[j] = (__bf16)pv;
     }
   };
-  auto mask = [&](int b) {
+  auto mask = [&](f32x16& Sb, int b) __attribute__((always_inline)) {
     const int qpos = qp0 + rw0 + l32;
     int last = Lk - 1;
     if (p.causal) last = min(last, qpos - kp0);
@@ -235,15 +284,15 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int off = (e >> 2) * 8 + (e & 3);
-      S[e] = off <= lim ? S[e] : -INFINITY;
+      Sb[e] = off <= lim ? Sb[e] : -INFINITY;
     }
   };
-  // raise the reference max of each row to the row max of S (rescaling acc and l)
-  auto settle_reference = [&]() {
-    float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);  // chains of 3-input max over the lane's 16 keys
+  // raise the reference max of each row to the row max of Sb (rescaling acc and l)
+  auto settle_reference = [&](const f32x16& Sb) __attribute__((always_inline)) {
+    float mx = fmaxf(fmaxf(Sb[0], Sb[1]), Sb[2]);  // chains of 3-input max over the lane's 16 keys
 #pragma unroll
-    for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, S[e]), S[e + 1]);
-    mx = fmaxf(mx, S[15]);
+    for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, Sb[e]), Sb[e + 1]);
+    mx = fmaxf(mx, Sb[15]);
     const float m_new = fmaxf(m_run, max_halves(mx) * c2);
     if (m_new > m_run) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was -inf
@@ -251,84 +300,158 @@ void fwd_bf16_kernel(FwdParams p) {
       acc[0] *= alpha;
       acc[1] *= alpha;
       m_run = m_new;
+      neg_m = -m_new;
     }
   };
 
-  // softmax of the scores of block b (keys 32b.. of the sequence chunk) -> P, l.
-  // Fast path: exponentials against the current reference max, kept when every
-  // lane-partial row sum is <= 2^8 (then no score exceeded the reference by more
-  // than 8 in log2 units, so p <= 256).  Otherwise - the row's first visible
-  // block (reference -inf, sums inf), or a score that outgrew the reference -
-  // the scores are recomputed (they are not kept live: registers), the
-  // reference is raised to the row max with acc and l rescaled, and the
-  // exponentials redone.
-  auto softmax = [&](auto masked_tag, auto buf_tag, auto half_tag, int b) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (MASKED) mask(b);
-    float rs;
-    exps(rs);
+  // One step of the software pipeline for block i (i % 4 == J, compile-time).
+  // The softmax of block i runs on the vector ALU while the matrix core does
+  // O += P V for block i-1 (first half) and S = K Q^T for block i+1 (second
+  // half); both are independent of block i, so one wave keeps both units fed.
+  //
+  // Exponentials are taken against the row's current reference max and kept
+  // when every lane-partial row sum is <= 2^8 (then no score exceeded the
+  // reference by more than 8 in log2 units, so p <= 256).  Otherwise - the
+  // row's first visible block (no reference yet), or a score that outgrew the
+  // reference - the block's scores are recomputed (they are not kept live:
+  // registers), the reference is raised to the row max with acc and l
+  // rescaled, and the exponentials redone.
+  //
+  // Buffers: block i's keys are read at step i-1 and its values at step i+1.
+  // At J == 3, between the two halves, all waves meet at the tile barrier: by
+  // then every wave has read the keys of this tile and the values of the tile
+  // before it, so the next-but-one tile is copied into those buffers.  The
+  // only later read of this tile's keys would be a recompute at J == 3, which
+  // therefore reads the keys from global memory.
+  auto step = [&](auto j_tag, int i) __attribute__((always_inline)) {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr int CUR = J & 1, NXT = CUR ^ 1;
+    const bool masked = i >= nfull;  // workgroup-uniform
+    if (masked) mask(S[CUR], i);
+    if constexpr (J == 1) advance_v(i >> 2);
+    float part[4];
+    // ---- first half: exponentials of keys 0..15 with O += V^T P^T of block i-1
+    {
+      bf16x8 va[4];
+      {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int db = 0; db < 2; ++db) va[2 * st + db] = vread(st, db, Int<(J + 3) & 3>{});
+      }
+      exps_half(S[CUR], P[CUR][0], part, Int<0>{});
+      {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[2 * st + db], P[NXT][st], acc[db], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // value reads
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // exp / fma / add / convert
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        }
+      }
+    }
+    if constexpr (J == 3) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's share of the next tile landed
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) k_addr[ks] ^= TILE_BYTES;
+      if ((i >> 2) + 2 < ntile) copy_tile((i >> 2) + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- second half: exponentials of keys 16..31 with S = K Q^T of block i+1
+    {
+      bf16x8 ka[4];
+      {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ka[ks] = kread(ks, Int<(J + 1) & 3>{});
+      }
+      exps_half(S[CUR], P[CUR][1], part, Int<1>{});
+      {
+        S[NXT] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          S[NXT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qr[ks], S[NXT], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // key reads
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float rs = (part[0] + part[1]) + (part[2] + part[3]);
     if (__builtin_amdgcn_ballot_w64(rs > SUM_LIMIT) != 0) {  // wave-uniform, rare
-      scores(buf_tag, half_tag);
-      if constexpr (MASKED) mask(b);
-      settle_reference();
-      exps(rs);
+      f32x16& Sb = S[CUR];
+      Sb = f32x16{};
+      if constexpr (J == 3) {
+        const int key = min(i * 32 + l32, Lk - 1);
+        const unsigned off = ((unsigned)(key * kstride) + half * 8) * 2u;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          Sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kgb + off + ks * 32),
+                                                       qr[ks], Sb, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          Sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<J>{}), qr[ks], Sb, 0, 0, 0);
+      }
+      if (masked) mask(Sb, i);
+      settle_reference(Sb);
+      exps_half(Sb, P[CUR][0], part, Int<0>{});
+      exps_half(Sb, P[CUR][1], part, Int<1>{});
+      rs = (part[0] + part[1]) + (part[2] + part[3]);
+      // the next block's scores are recomputed too, so they need no registers
+      // while this path runs
+      {
+        S[NXT] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          S[NXT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<(J + 1) & 3>{}), qr[ks], S[NXT], 0, 0, 0);
+      }
     }
     l_run += rs;
   };
-  // O^T += V^T P^T for the block in quarter `half_tag` of LDS buffer `buf_tag`
-  auto pv = [&](auto buf_tag, auto half_tag) {
-    constexpr int VBASE = (decltype(buf_tag)::value * TILE_ELEMS + decltype(half_tag)::value * 32 * D) * 2;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const __attribute__((address_space(3))) char* vb =
-            (const __attribute__((address_space(3))) char*)lds_v0 + v_lane[db] + VBASE + st * 16 * D * 2;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * D * 2));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[st], acc[db], 0, 0, 0);
-      }
-    }
-  };
-  // One block of a tile.  Once the exponentials of block b have consumed the
-  // scores, the scores of the tile's next block are issued into the same
-  // registers BEFORE O += P V of block b, so the matrix core finishes them
-  // first and the next softmax overlaps the P V products.
-  auto block = [&](auto masked_tag, auto buf_tag, auto half_tag, int b) {
-    softmax(masked_tag, buf_tag, half_tag, b);
-    constexpr int H = decltype(half_tag)::value;
-    if constexpr (H + 1 < BPT) scores(buf_tag, Int<H + 1>{});
-    pv(buf_tag, half_tag);
-  };
-
-  // blocks [0, nfull) are visible to every row of the tile; later ones need the mask
-  const int nfull = min(nblk, kfull >> 5);
-  // one tile: it has landed in buffer BUF (own copies waited for, then the
-  // barrier); every wave is done with the other buffer, which takes tile t+1
-  auto tile_step = [&](auto buf_tag, int t) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+  // ---- prologue: tile 0 landed, tile 1 in flight, scores of block 0.
+  // Step 0 also multiplies the values of block 3 of tile 0 by an all-zero P
+  // (there is no block -1), and the last step computes scores of a block past
+  // the end from whatever the key buffer holds; both results are unused.
+  P[1][0] = bf16x8{};
+  P[1][1] = bf16x8{};
+  if (nblk > 0) {
+    copy_tile(0);
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the queries and this wave's share of tile 0
     __syncthreads();
-    if (t + 1 < ntile) copy_tile(t + 1, BUF ^ 1);
-    const int b0 = t * BPT;
-    scores(buf_tag, Int<0>{});
-    if (b0 + 3 < nfull) {
-      block(MaskTag<false>{}, buf_tag, Int<0>{}, b0);
-      block(MaskTag<false>{}, buf_tag, Int<1>{}, b0 + 1);
-      block(MaskTag<false>{}, buf_tag, Int<2>{}, b0 + 2);
-      block(MaskTag<false>{}, buf_tag, Int<3>{}, b0 + 3);
-    } else {
-      if (b0 < nfull) block(MaskTag<false>{}, buf_tag, Int<0>{}, b0); else block(MaskTag<true>{}, buf_tag, Int<0>{}, b0);
-      if (b0 + 1 < nfull) block(MaskTag<false>{}, buf_tag, Int<1>{}, b0 + 1); else if (b0 + 1 < nblk) block(MaskTag<true>{}, buf_tag, Int<1>{}, b0 + 1);
-      if (b0 + 2 < nfull) block(MaskTag<false>{}, buf_tag, Int<2>{}, b0 + 2); else if (b0 + 2 < nblk) block(MaskTag<true>{}, buf_tag, Int<2>{}, b0 + 2);
-      if (b0 + 3 < nblk) block(MaskTag<true>{}, buf_tag, Int<3>{}, b0 + 3);
-    }
+    if (ntile > 1) copy_tile(1);
+    S[0] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<0>{}), qr[ks], S[0], 0, 0, 0);
+  }
+  // O += V^T P^T of the last block (its step J did not advance the value buffer if J == 0)
+  auto last_pv = [&](auto j_tag, int i) __attribute__((always_inline)) {
+    constexpr int J = decltype(j_tag)::value;
+    if constexpr (J == 0) advance_v(i >> 2);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(st, db, Int<J>{}), P[J & 1][st], acc[db], 0, 0, 0);
   };
-  if (ntile > 0) copy_tile(0, 0);
-  for (int t = 0; t < ntile; t += 2) {
-    tile_step(Int<0>{}, t);
-    if (t + 1 < ntile) tile_step(Int<1>{}, t + 1);
+  if (nblk > 0) {
+    for (int i0 = 0; i0 < nblk; i0 += 4) {
+      step(Int<0>{}, i0);
+      step(Int<1>{}, i0 + 1);
+      step(Int<2>{}, i0 + 2);
+      step(Int<3>{}, i0 + 3);
+    }
+    last_pv(Int<3>{}, 0);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2

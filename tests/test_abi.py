@@ -94,6 +94,8 @@ def _step(p, dtype=0, ptrs=None, launched=True):
     (dict(num_seqs=2, cu_q=[0, 64, 127], cu_k=[0, 64, 128]), 1, "total"),
     (dict(q_pos0=[-3]), 1, "negative"),
     (dict(k_pos0=[2**31 - 10]), 1, "overflow"),
+    # bf16 keys of one sequence: 2**21 rows x 8 heads x 64 x 2 B = 2 GiB
+    (dict(total_k=2**21, num_q_heads=8, num_kv_heads=8, causal=0), 2, "2 GiB"),
 ])
 def test_invalid_problem_is_rejected_before_launch(kw, expect, needle):
     p, keep = _prob(**kw)
