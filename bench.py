@@ -43,6 +43,8 @@ def parse_args():
                     help="comma list of further workloads measured in the same run ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="merge each ring step with the separate merge kernel instead of in the step")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows of the oracle sample (all heads, all ring steps)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -65,7 +67,7 @@ def kernel_source_hash() -> str:
 class Job:
     """One workload with its inputs resident on the device and a run() for one step."""
 
-    def __init__(self, name):
+    def __init__(self, name, fused=True):
         import torch
 
         from ring_attention_03_amd import RingAttention, RingLayout
@@ -73,6 +75,7 @@ class Job:
 
         self.w = w = WORKLOADS[name]
         self.name = name
+        self.fused = fused
         q, k, v = make_qkv(w)
         self.cpu_inputs = (q, k, v)
         dev = torch.device("cuda:0")
@@ -91,7 +94,8 @@ class Job:
         tq, hq, d = self.q.shape
         self.o = torch.empty(tq, hq, d, device=dev)
         self.lse = torch.empty(hq, tq, device=dev)
-        if w.n_chunks > 1:
+        self.o_p = self.lse_p = None
+        if w.n_chunks > 1 and not fused:
             self.o_p, self.lse_p = torch.empty_like(self.o), torch.empty_like(self.lse)
         self.pairs = lay.visible_pairs(self.rank)
         self.flops = 4 * w.head_dim * w.num_q_heads * self.pairs
@@ -111,14 +115,16 @@ class Job:
                 e.record()
                 events.append(("step", s, e))
             return 1
-        return self.ring.run(self.q, self.chunks, self.o, self.lse, self.o_p, self.lse_p, events=events)
+        return self.ring.run(self.q, self.chunks, self.o, self.lse, self.o_p, self.lse_p, events=events,
+                             fused=self.fused)
 
     def config(self):
         w = self.w
         return {"workload": self.name, "seq_lens": list(w.seqlens), "ring_chunks": w.n_chunks,
                 "rank": self.rank, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                 "head_dim": w.head_dim, "causal": True, "local_q_rows": int(self.q.shape[0]),
-                "algorithmic_tflop": self.flops / 1e12}
+                "algorithmic_tflop": self.flops / 1e12,
+                "merge": "in the step kernel" if self.fused else "separate merge kernel"}
 
 
 def time_job(job, steps, warmup):
@@ -300,7 +306,7 @@ def main():
     log = lambda m: print(m, file=sys.stderr, flush=True)  # noqa: E731
 
     log(f"bench: preparing {args.workload}")
-    job = Job(args.workload)
+    job = Job(args.workload, fused=not args.unfused)
     wall, per_kind = time_job(job, args.steps, args.warmup)
     main_res = summarize(job, args.steps, wall, per_kind)
     log(f"bench: {args.workload}: {main_res['ms_per_step']:.3f} ms/step, {main_res['tflops']:.1f} TFLOP/s "
@@ -309,7 +315,7 @@ def main():
     extra = {}
     for name in [x for x in args.extra.split(",") if x and x != args.workload]:
         log(f"bench: preparing {name}")
-        ej = Job(name)
+        ej = Job(name, fused=not args.unfused)
         ew, epk = time_job(ej, args.extra_steps, 1)
         extra[name] = summarize(ej, args.extra_steps, ew, epk)
         extra[name]["algorithmic_tflop"] = ej.flops / 1e12

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 #define ATTN_MAX_SEQS 64 /* packed sequences per call (their tables travel in kernel arguments) */
 
 typedef enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_FP32 = 1 } attn_dtype;
@@ -103,6 +103,25 @@ attn_status attn_ring_step(const attn_problem* problem, attn_dtype dtype,
                            const void* q, const void* k, const void* v,
                            float* o_part, float* lse_part,
                            int32_t* launched, hipStream_t stream);
+
+/*
+ * One ring step fused with its merge: attention of the local query rows
+ * against one key/value block, folded by log-sum-exp straight into the
+ * running state (o_acc, lse_acc) in place.  The result equals attn_ring_step
+ * into separate buffers followed by attn_ring_merge (up to rounding), without
+ * the partial buffers or the second pass over them.
+ *
+ * o_acc [total_q, Hq, head_dim] and lse_acc [Hq, total_q] are fp32, read and
+ * written; they must hold a valid running state (finite O; a row with no keys
+ * yet is (0, -inf)).  Rows that see no key in this block are left untouched;
+ * a block with no visible key at all enqueues nothing.  *launched (if
+ * non-NULL) is 1 when a kernel was enqueued, else 0.  Alignment and overlap
+ * rules are those of attn_ring_step.
+ */
+attn_status attn_ring_step_merge(const attn_problem* problem, attn_dtype dtype,
+                                 const void* q, const void* k, const void* v,
+                                 float* o_acc, float* lse_acc,
+                                 int32_t* launched, hipStream_t stream);
 
 /*
  * Merge of two partial results over disjoint key sets (the step that lets the

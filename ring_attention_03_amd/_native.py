@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnring
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_DTYPE_BF16, ATTN_DTYPE_FP32 = 0, 1
 MAX_SEQS = 64
-EXPORTED = ("attn_ring_step", "attn_ring_merge", "attn_prefill_causal", "attn_last_error",
-            "attn_abi_version")
+ABI_VERSION = 2
+EXPORTED = ("attn_ring_step", "attn_ring_step_merge", "attn_ring_merge", "attn_prefill_causal",
+            "attn_last_error", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -60,6 +61,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_ring_step.argtypes = [ctypes.POINTER(AttnProblem), ctypes.c_int, vp, vp, vp, vp, vp,
                                    ctypes.POINTER(ctypes.c_int32), vp]
     lib.attn_ring_step.restype = ctypes.c_int
+    lib.attn_ring_step_merge.argtypes = [ctypes.POINTER(AttnProblem), ctypes.c_int, vp, vp, vp, vp,
+                                         vp, ctypes.POINTER(ctypes.c_int32), vp]
+    lib.attn_ring_step_merge.restype = ctypes.c_int
     lib.attn_prefill_causal.argtypes = [ctypes.POINTER(AttnProblem), ctypes.c_int, vp, vp, vp, vp,
                                         vp, vp]
     lib.attn_prefill_causal.restype = ctypes.c_int
@@ -69,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
     lib.attn_abi_version.restype = ctypes.c_int32
+    if lib.attn_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.attn_abi_version()}, expected {ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -149,6 +155,27 @@ def attn_ring_step(q, k, v, o_part, lse_part, *, cu_q=None, cu_k=None, q_pos0=No
                               ctypes.byref(launched) if report_skip else None, _stream(stream)))
     del keep
     return bool(launched.value) if report_skip else True
+
+
+def attn_ring_step_merge(q, k, v, o_acc, lse_acc, *, cu_q=None, cu_k=None, q_pos0=None,
+                         k_pos0=None, scale=0.0, causal=True, stream=None) -> bool:
+    """One ring step folded into the running state (see ``attn_ring_step_merge`` in attnring.h).
+
+    Returns whether a kernel was enqueued (False: no key of this block is
+    visible, and the state is unchanged).
+    """
+    lib = load_library()
+    _require_device(q, k, v, o_acc, lse_acc)
+    _check_inputs(q, k, v)
+    _check_out_shapes(q, o_acc, lse_acc)
+    prob, keep = make_problem(q, k, cu_q=cu_q, cu_k=cu_k, q_pos0=q_pos0, k_pos0=k_pos0,
+                              scale=scale, causal=causal)
+    launched = ctypes.c_int32(0)
+    _check(lib.attn_ring_step_merge(ctypes.byref(prob), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(o_acc), _ptr(lse_acc), ctypes.byref(launched),
+                                    _stream(stream)))
+    del keep
+    return bool(launched.value)
 
 
 def attn_prefill_causal(q, k, v, o, lse, *, cu_seqlens=None, scale=0.0, stream=None) -> None:

@@ -218,6 +218,20 @@ attn_status attn_ring_step(const attn_problem* problem, attn_dtype dtype, const 
   return st;
 }
 
+attn_status attn_ring_step_merge(const attn_problem* problem, attn_dtype dtype, const void* q,
+                                 const void* k, const void* v, float* o_acc, float* lse_acc,
+                                 int32_t* launched, hipStream_t stream) {
+  if (launched) *launched = 0;
+  Plan plan;
+  attn_status st = plan_forward(problem, dtype, q, k, v, o_acc, lse_acc, &plan);
+  if (st != ATTN_OK) return st;
+  if (plan.n_units == 0 || !plan.any_visible) return ok();  // merging the identity: nothing to do
+  plan.p.merge = 1;
+  st = launch_forward(plan, dtype, stream);
+  if (st == ATTN_OK && launched) *launched = 1;
+  return st;
+}
+
 attn_status attn_prefill_causal(const attn_problem* problem, attn_dtype dtype, const void* q,
                                 const void* k, const void* v, float* o, float* lse,
                                 hipStream_t stream) {

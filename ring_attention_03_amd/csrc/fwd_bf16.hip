@@ -46,6 +46,7 @@
 // normalised with the same reference, so the result does not depend on which
 // reference was used.
 #include "kernels.h"
+#include "merge_math.h"
 
 namespace attnring {
 namespace {
@@ -249,6 +250,10 @@ void fwd_bf16_kernel(FwdParams p) {
   float neg_m = 3.0e38f;
   float l_run = 0.f;        // lane-partial sum of 2^(s*c - m_run)
   const float c2 = p.scale_log2;
+  // Make the scalar load of c2 complete here: otherwise its wait (lgkmcnt,
+  // shared with LDS reads) lands inside the loop, where the first use is, and
+  // drains every LDS read in flight at the top of each iteration.
+  asm volatile("" ::"s"(c2));
   f32x16 S[2];              // scores of blocks i (S[i&1]) and i+1: keys x this wave's 32 queries
   bf16x8 P[2][2];           // bf16 probabilities of blocks i and i-1 ([i&1]), per 16-key step
 
@@ -454,27 +459,46 @@ void fwd_bf16_kernel(FwdParams p) {
     last_pv(Int<3>{}, 0);
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; written, or merged into
+  // the running state (o, lse) by their log-sum-exps (rows that saw no key here
+  // leave the state as it is)
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int row = rw0 + l32;
   if (row < Lq) {
     const size_t grow = (size_t)(p.q_row0[s] + row);
     float* dst = p.o + (grow * p.hq + head) * D + half * 4;
+    float* lse_dst = p.lse + (size_t)head * p.total_q + grow;
+    const float lse_b = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    if (!p.merge) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v4;
-        v4[0] = acc[db][i * 4 + 0] * inv;
-        v4[1] = acc[db][i * 4 + 1] * inv;
-        v4[2] = acc[db][i * 4 + 2] * inv;
-        v4[3] = acc[db][i * 4 + 3] * inv;
-        *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = v4;
-      }
-    if (half == 0) {
-      const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-      p.lse[(size_t)head * p.total_q + grow] = lse;
+        for (int i = 0; i < 4; ++i) {
+          f32x4 v4;
+          v4[0] = acc[db][i * 4 + 0] * inv;
+          v4[1] = acc[db][i * 4 + 1] * inv;
+          v4[2] = acc[db][i * 4 + 2] * inv;
+          v4[3] = acc[db][i * 4 + 3] * inv;
+          *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = v4;
+        }
+      if (half == 0) *lse_dst = lse_b;
+    } else if (l_tot > 0.f) {
+      float lse, wa, wb;
+      lse_merge_weights(*lse_dst, lse_b, &lse, &wa, &wb);  // both halves read before half 0 writes
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 ob;
+          ob[0] = acc[db][i * 4 + 0] * inv;
+          ob[1] = acc[db][i * 4 + 1] * inv;
+          ob[2] = acc[db][i * 4 + 2] * inv;
+          ob[3] = acc[db][i * 4 + 3] * inv;
+          f32x4* o4 = reinterpret_cast<f32x4*>(dst + db * 32 + i * 8);
+          *o4 = wa * *o4 + wb * ob;
+        }
+      if (half == 0) *lse_dst = lse;
     }
   }
 }

@@ -7,6 +7,7 @@
 // staged in LDS and read as broadcasts, an online softmax in base 2 with fp32
 // throughout.
 #include "kernels.h"
+#include "merge_math.h"
 
 namespace attnring {
 namespace {
@@ -100,15 +101,31 @@ __global__ __launch_bounds__(ROWS) void fwd_f32_kernel(FwdParams p) {
   }
 
   if (valid) {
+    // O = acc / l, LSE = (m + log2 l) * ln 2: written, or merged into the running
+    // state (o, lse) by log-sum-exp (rows that saw no key here leave it as it is)
     const size_t grow = (size_t)(p.q_row0[s] + row);
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     float* dst = p.o + (grow * p.hq + head) * D;
+    float* lse_dst = p.lse + (size_t)head * p.total_q + grow;
+    const float lse_b = l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+    if (!p.merge) {
 #pragma unroll
-    for (int i = 0; i < D; i += 4)
-      *reinterpret_cast<float4*>(dst + i) =
-          make_float4(acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv);
-    p.lse[(size_t)head * p.total_q + grow] =
-        l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+      for (int i = 0; i < D; i += 4)
+        *reinterpret_cast<float4*>(dst + i) =
+            make_float4(acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv);
+      *lse_dst = lse_b;
+    } else if (l_run > 0.f) {
+      float lse, wa, wb;
+      lse_merge_weights(*lse_dst, lse_b, &lse, &wa, &wb);
+#pragma unroll
+      for (int i = 0; i < D; i += 4) {
+        float4* o4 = reinterpret_cast<float4*>(dst + i);
+        const float4 a = *o4;
+        const float4 b = make_float4(acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv);
+        *o4 = make_float4(wa * a.x + wb * b.x, wa * a.y + wb * b.y, wa * a.z + wb * b.z, wa * a.w + wb * b.w);
+      }
+      *lse_dst = lse;
+    }
   }
 }
 

@@ -22,6 +22,7 @@ struct FwdParams {
   int32_t hq;
   int32_t hkv;
   int32_t causal;
+  int32_t merge;     // 1: fold this block's result into (o, lse) in place instead of writing it
   float scale_log2;  // softmax scale times log2(e): scores are exponentiated base 2
   int32_t nseq;
   int32_t n_head_groups;  // workgroups per row tile (one per group of heads sharing K/V)

@@ -13,6 +13,7 @@
 // lane that writes the new LSE belongs to the same wave as the lanes that
 // read the old one (no cross-wave race on the in-place update).
 #include "kernels.h"
+#include "merge_math.h"
 
 namespace attnring {
 namespace {
@@ -31,18 +32,8 @@ __global__ __launch_bounds__(THREADS) void merge_kernel(int32_t total_q, int32_t
   const int64_t q = rh / hq;
   const int h = (int)(rh - q * hq);
   const int64_t li = (int64_t)h * total_q + q;
-  const float la = lse_acc[li], lb = lse_part[li];
-  const float mx = fmaxf(la, lb);
   float lse, wa, wb;
-  if (mx == -INFINITY) {
-    lse = -INFINITY;
-    wa = 0.f;
-    wb = 0.f;
-  } else {
-    lse = mx + logf(expf(la - mx) + expf(lb - mx));
-    wa = expf(la - lse);
-    wb = expf(lb - lse);
-  }
+  lse_merge_weights(lse_acc[li], lse_part[li], &lse, &wa, &wb);
   const int64_t oi = rh * LANES_PER_ROW + sub;
   const f32x4 a = o_acc[oi], b = o_part[oi];
   o_acc[oi] = wa * a + wb * b;

@@ -79,14 +79,16 @@ def ring_chunk(rank: int, step: int, n_chunks: int) -> int:
 
 
 class RingAttention:
-    """Runs device ``rank``'s ring: N steps of attention and LSE merges into (o, lse).
+    """Runs device ``rank``'s ring: N steps of attention merged by LSE into (o, lse).
 
     ``q_local`` is the device's packed query chunk; ``kv_chunks[j]`` is the
     packed (k, v) of chunk j, already in device memory.  The first step that
     has visible keys writes straight into the running state (merging into the
-    identity would give the same bits); every later active step writes the
-    partial buffers and is folded in by ``attn_ring_merge``.  Fully masked
-    steps launch nothing.
+    identity would give the same result); every later active step is folded
+    in by log-sum-exp.  By default the fold happens in the step kernel's
+    epilogue (``attn_ring_step_merge``); with ``o_part``/``lse_part`` given and
+    ``fused=False`` each step writes the partial buffers and
+    ``attn_ring_merge`` folds them in.  Fully masked steps launch nothing.
     """
 
     def __init__(self, layout: RingLayout, rank: int, scale: float = 0.0):
@@ -96,14 +98,16 @@ class RingAttention:
         self.rank = rank
         self.scale = scale
 
-    def run(self, q_local, kv_chunks, o_acc, lse_acc, o_part, lse_part, stream=None,
-            events=None) -> int:
+    def run(self, q_local, kv_chunks, o_acc, lse_acc, o_part=None, lse_part=None, stream=None,
+            events=None, fused=True) -> int:
         """Run the ring; returns the number of steps that launched work.
 
         ``events``, if a list, receives ``(kind, start, end)`` timing events
         (kind "step" or "merge") recorded on the launch stream around every
         launch, for per-kernel timing.
         """
+        if not fused and (o_part is None or lse_part is None):
+            raise ValueError("the unfused ring needs o_part and lse_part")
         lay, r = self.layout, self.rank
         timed = _EventTimer(events, stream)
         cu = lay.cu
@@ -113,17 +117,22 @@ class RingAttention:
         for t in range(lay.n_chunks):
             j = ring_chunk(r, t, lay.n_chunks)
             k_j, v_j = kv_chunks[j]
-            dst = (o_part, lse_part) if wrote_state else (o_acc, lse_acc)
+            kw = dict(cu_q=cu, cu_k=cu, q_pos0=q_pos0, k_pos0=lay.pos0(j), scale=self.scale,
+                      causal=True, stream=stream)
             with timed("step") as mark:
-                launched = _native.attn_ring_step(q_local, k_j, v_j, *dst, cu_q=cu, cu_k=cu,
-                                                  q_pos0=q_pos0, k_pos0=lay.pos0(j),
-                                                  scale=self.scale, causal=True,
-                                                  report_skip=True, stream=stream)
+                if not wrote_state:
+                    launched = _native.attn_ring_step(q_local, k_j, v_j, o_acc, lse_acc,
+                                                      report_skip=True, **kw)
+                elif fused:
+                    launched = _native.attn_ring_step_merge(q_local, k_j, v_j, o_acc, lse_acc, **kw)
+                else:
+                    launched = _native.attn_ring_step(q_local, k_j, v_j, o_part, lse_part,
+                                                      report_skip=True, **kw)
                 mark(launched)
             if not launched:
                 continue
             active += 1
-            if wrote_state:
+            if wrote_state and not fused:
                 with timed("merge") as mark:
                     _native.attn_ring_merge(o_acc, lse_acc, o_part, lse_part, stream=stream)
                     mark(True)

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = _native.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == _native.ABI_VERSION == 2
     assert lib.attn_last_error() is not None
 
 
@@ -103,6 +103,30 @@ def test_invalid_problem_is_rejected_before_launch(kw, expect, needle):
     assert st == expect, msg
     assert needle in msg
     assert launched == 0
+    del keep
+
+
+@no_gpu_only
+def test_step_merge_validates_like_the_step():
+    lib = _native.load_library()
+
+    def call(p, ptrs=(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5)):
+        flag = ctypes.c_int32(-1)
+        st = lib.attn_ring_step_merge(ctypes.byref(p), 0, *ptrs, ctypes.byref(flag), None)
+        return st, flag.value, lib.attn_last_error().decode()
+
+    p, keep = _prob(num_kv_heads=3)
+    st, launched, msg = call(p)
+    assert st == 1 and launched == 0 and "multiple" in msg
+    p, keep = _prob(head_dim=128)
+    assert call(p)[0] == 2
+    p, keep = _prob()
+    st, _, msg = call(p, ptrs=(FAKE, FAKE * 100, FAKE * 200, FAKE + 64, FAKE * 300))
+    assert st == 1 and "overlap" in msg
+    # a block wholly in the future: valid, nothing to merge, nothing enqueued
+    p, keep = _prob(q_pos0=[0], k_pos0=[1000])
+    st, launched, _ = call(p)
+    assert st == 0 and launched == 0
     del keep
 
 

@@ -19,7 +19,7 @@ import torch
 
 from oracle import attention_ref, causal_attention_ref, merge_ref, ring_ref
 from ring_attention_03_amd import (AttnError, RingAttention, RingLayout, attn_prefill_causal,
-                                   attn_ring_merge, attn_ring_step)
+                                   attn_ring_merge, attn_ring_step, attn_ring_step_merge)
 from ring_attention_03_amd.workloads import WORKLOADS, make_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -32,7 +32,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_ring(q, k, v, seqlens, n, rank, scale=0.0):
+def run_ring(q, k, v, seqlens, n, rank, scale=0.0, fused=True):
     """Run device ``rank``'s ring on the GPU from full packed CPU tensors; returns CPU (O, LSE)."""
     lay = RingLayout(tuple(seqlens), n)
     dev = "cuda"
@@ -43,7 +43,7 @@ def run_ring(q, k, v, seqlens, n, rank, scale=0.0):
     o = torch.empty(tq, hq, d, device=dev)
     lse = torch.empty(hq, tq, device=dev)
     o_p, lse_p = torch.empty_like(o), torch.empty_like(lse)
-    RingAttention(lay, rank, scale).run(q_local, chunks, o, lse, o_p, lse_p)
+    RingAttention(lay, rank, scale).run(q_local, chunks, o, lse, o_p, lse_p, fused=fused)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
@@ -246,6 +246,59 @@ def test_merge_kernel_matches_oracle():
     torch.cuda.synchronize()
     o_ref, l_ref = merge_ref(oa, la, ob, lb)
     assert_close(o_acc.cpu(), l_acc.cpu(), o_ref, l_ref, 1e-5, 1e-5, "merge")
+
+
+@pytest.mark.parametrize("seqlens,n,hq,hkv,vd", [RING_CASES[0], RING_CASES[3]])
+def test_fused_merge_ring_matches_unfused_ring(seqlens, n, hq, hkv, vd):
+    # the merge folded into the step epilogue computes the same log-sum-exp
+    # combination as the separate merge kernel: only rounding may differ
+    w = WORKLOADS["ring_64k_rank7"].scaled(seqlens=seqlens, n_chunks=n, num_q_heads=hq,
+                                           num_kv_heads=hkv, v_dist=vd, seed=21)
+    q, k, v = make_qkv(w)
+    for r in range(n):
+        log(f"fused vs unfused ring {seqlens} N={n} rank {r}")
+        o_f, lse_f = run_ring(q, k, v, seqlens, n, r, fused=True)
+        o_u, lse_u = run_ring(q, k, v, seqlens, n, r, fused=False)
+        assert torch.equal(torch.isneginf(lse_f), torch.isneginf(lse_u))
+        fin = torch.isfinite(lse_u)
+        assert float((o_f - o_u).abs().max()) <= 1e-5
+        assert float((lse_f[fin] - lse_u[fin]).abs().max()) <= 1e-5
+        o_ref, lse_ref = ring_ref(q, k, v, seqlens, n, r)
+        assert_close(o_f, lse_f, o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, f"fused rank {r}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_step_merge_folds_a_block_into_the_state(dtype):
+    # running state from one key block (positions 0..89), then a second block
+    # (positions 90..199) folded in by the fused step; queries at 40..229, so
+    # the first 50 rows see no key of the second block and must stay untouched
+    g = torch.Generator().manual_seed(22)
+    tq, hq, hkv = 190, 8, 2
+    q = torch.randn(tq, hq, 64, generator=g).to(dtype)
+    k = torch.randn(200, hkv, 64, generator=g).to(dtype)
+    v = torch.randn(200, hkv, 64, generator=g).to(dtype)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty(tq, hq, 64, device="cuda")
+    lse = torch.empty(hq, tq, device="cuda")
+    assert attn_ring_step(qd, kd[:90], vd[:90], o, lse, q_pos0=[40], k_pos0=[0])
+    torch.cuda.synchronize()
+    o_before, lse_before = o.clone(), lse.clone()
+    assert attn_ring_step_merge(qd, kd[90:].contiguous(), vd[90:].contiguous(), o, lse,
+                                q_pos0=[40], k_pos0=[90])
+    torch.cuda.synchronize()
+    assert torch.equal(o[:50], o_before[:50]) and torch.equal(lse[:, :50], lse_before[:, :50])
+    oa, la = attention_ref(q, k[:90], v[:90], q_pos0=[40], k_pos0=[0])
+    ob, lb = attention_ref(q, k[90:], v[90:], q_pos0=[40], k_pos0=[90])
+    o_ref, lse_ref = merge_ref(oa, la, ob, lb)
+    full_o, full_lse = attention_ref(q, k, v, q_pos0=[40], k_pos0=[0])  # and that is full attention
+    assert np.abs(o_ref - full_o).max() < 1e-12 and np.abs(lse_ref - full_lse).max() < 1e-12
+    tol = (O_TOL_BF16, LSE_TOL_BF16) if dtype == torch.bfloat16 else (TOL_F32, TOL_F32)
+    assert_close(o.cpu(), lse.cpu(), o_ref, lse_ref, *tol, f"step merge {dtype}")
+    # a block wholly in the future of every row enqueues nothing and changes nothing
+    o_before, lse_before = o.clone(), lse.clone()
+    assert not attn_ring_step_merge(qd, kd, vd, o, lse, q_pos0=[40], k_pos0=[400])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_before) and torch.equal(lse, lse_before)
 
 
 def test_deterministic():

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from oracle import chunk_layout_ref, visible_pairs_ref
-from ring_attention_03_amd.ring import RingLayout, ring_chunk
+from ring_attention_03_amd.ring import RingAttention, RingLayout, ring_chunk
 from ring_attention_03_amd.workloads import WORKLOADS, make_qkv, sample_rows
 
 
@@ -58,3 +58,53 @@ def test_workload_recipe_is_seeded_and_shaped():
     assert vu.dtype == torch.bfloat16 and vu.float().abs().max() <= 1.0
     rows = sample_rows(1000, 20, 3)
     assert rows[:8] == list(range(8)) and rows[-8:] == list(range(992, 1000))
+
+
+class _FakeNative:
+    """Records the ring's library calls; a step "sees keys" when its chunk is not in the future."""
+
+    def __init__(self, rank):
+        self.rank = rank
+        self.calls = []
+
+    def _visible(self, k_pos0, q_pos0):
+        return k_pos0[0] <= q_pos0[0]
+
+    def attn_ring_step(self, q, k, v, o, lse, *, q_pos0, k_pos0, report_skip=True, **kw):
+        self.calls.append(("step", o, k_pos0[0]))
+        return self._visible(k_pos0, q_pos0) or not report_skip
+
+    def attn_ring_step_merge(self, q, k, v, o, lse, *, q_pos0, k_pos0, **kw):
+        self.calls.append(("step_merge", o, k_pos0[0]))
+        return self._visible(k_pos0, q_pos0)
+
+    def attn_ring_merge(self, o_acc, lse_acc, o_part, lse_part, **kw):
+        self.calls.append(("merge", o_acc, None))
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_ring_driver_call_sequence(monkeypatch, fused):
+    from ring_attention_03_amd import ring as ring_mod
+
+    n, rank, c = 4, 2, 8
+    fake = _FakeNative(rank)
+    monkeypatch.setattr(ring_mod, "_native", fake)
+    lay = RingLayout((n * c,), n)
+    acc, part = "acc", "part"
+    chunks = [(f"k{j}", f"v{j}") for j in range(n)]
+    active = RingAttention(lay, rank).run("q", chunks, acc, "lse", part, "lse_part", fused=fused)
+    # ring order from rank 2: chunks 2, 1, 0, 3 (positions 16, 8, 0, 24); chunk 3 is in the future
+    assert active == 3
+    kinds = [(kind, buf, pos) for kind, buf, pos in fake.calls]
+    if fused:
+        assert kinds == [("step", acc, 16), ("step_merge", acc, 8), ("step_merge", acc, 0),
+                         ("step_merge", acc, 24)]
+    else:
+        assert kinds == [("step", acc, 16), ("step", part, 8), ("merge", acc, None),
+                         ("step", part, 0), ("merge", acc, None), ("step", part, 24)]
+
+
+def test_unfused_ring_needs_partial_buffers():
+    lay = RingLayout((32,), 4)
+    with pytest.raises(ValueError):
+        RingAttention(lay, 1).run("q", [("k", "v")] * 4, "acc", "lse", fused=False)
