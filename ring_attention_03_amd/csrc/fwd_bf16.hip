@@ -74,9 +74,13 @@ constexpr int TILE_BYTES = TILE_ELEMS * 2;
 constexpr float SUM_LIMIT = 256.0f;  // a block's exponentials are kept when each lane-partial sum is <= 2^8
 
 // LDS tile layout: row-major [key][64], 16-byte chunks XOR-swizzled per row so
-// that the MFMA operand reads hit distinct banks (K: 16-byte reads of 8
-// consecutive rows; V: transposing reads of 4 consecutive rows x 32 bytes).
-__device__ __forceinline__ int k_pos(int key, int chunk) { return chunk ^ (key & 7); }
+// that the MFMA operand reads hit distinct banks.  The LDS serves 256 bytes
+// (64 banks) per clock, so a 16-byte read is conflict-free when each group of
+// 16 lanes covers all of them: the K reads (lane = key row) take 16
+// consecutive rows, two rows per 256 bytes, so the K chunk is XORed with
+// bits 1-3 of the row; the transposing V reads take 4 consecutive rows x 32
+// bytes per 16 lanes, so the V chunk pair is XORed with the row's low 2 bits.
+__device__ __forceinline__ int k_pos(int key, int chunk) { return chunk ^ ((key >> 1) & 7); }
 __device__ __forceinline__ int v_pos(int key, int chunk) { return chunk ^ ((key & 3) << 1); }
 __device__ __forceinline__ int k_off(int key, int chunk) { return key * D + (k_pos(key, chunk) << 3); }
 __device__ __forceinline__ int v_off(int key, int chunk) { return key * D + (v_pos(key, chunk) << 3); }
@@ -184,7 +188,7 @@ void fwd_bf16_kernel(FwdParams p) {
   // ---- tile copy HBM -> LDS: 16-byte slot i of a tile (lane-linear per wave and
   // instruction) is (key row i/8, position i%8) and holds global chunk
   // position ^ swizzle(row).  A pass of the workgroup fills NW*64 slots (NW*8
-  // rows, a multiple of 8, so every pass sees the same swizzle); keys past the
+  // rows, a multiple of 16, so every pass sees the same swizzle); keys past the
   // end read the last row instead (finite data, masked out of the scores).
   constexpr int ROWS_PER_PASS = NW * 8;
   constexpr int PASSES = BT / ROWS_PER_PASS;
@@ -195,24 +199,41 @@ void fwd_bf16_kernel(FwdParams p) {
   const char* vgb = reinterpret_cast<const char*>(reinterpret_cast<const unsigned short*>(p.v) + kv_base);
   // Per-lane byte offsets stay 32-bit (the host bounds a sequence's K/V to 2 GiB),
   // so the copies use a scalar base plus one vector offset.
-  const unsigned k_lane_off = (slot_pos ^ (slot_key & 7)) << 4;         // bytes within a key row
-  const unsigned v_lane_off = (slot_pos ^ ((slot_key & 3) << 1)) << 4;
-  const unsigned lds_wave = (unsigned)(uintptr_t)(const lds_u16*)(const unsigned short*)lds + wave * 1024;
+  const unsigned k_lane_off = (unsigned)k_pos(slot_key, slot_pos) << 4;  // bytes within a key row
+  const unsigned v_lane_off = (unsigned)v_pos(slot_key, slot_pos) << 4;
+  // this wave's LDS byte address within a pass, wave-uniform
+  const unsigned lds_wave = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(const lds_u16*)(const unsigned short*)lds + wave * 1024);
+  // per-lane source offsets of a tile's first pass; a tile or pass adds a
+  // wave-uniform amount to the scalar base instead
+  const unsigned k_src = (unsigned)(slot_key * kstride) * 2u + k_lane_off;
+  const unsigned v_src = (unsigned)(slot_key * kstride) * 2u + v_lane_off;
+  const unsigned pass_bytes = (unsigned)(ROWS_PER_PASS * kstride) * 2u;
   auto copy_tile = [&](int t) __attribute__((always_inline)) {
     const unsigned kb = (t % NKB) * TILE_BYTES, vb = (NKB + t % NVB) * TILE_BYTES;
+    if (t * BT + BT <= Lk) {  // every key of the tile exists: no clamping
+      const size_t tile_off = (size_t)(t * BT) * kstride * 2;
 #pragma unroll
-    for (int j = 0; j < PASSES; ++j) {
-      const int key = min(t * BT + j * ROWS_PER_PASS + slot_key, Lk - 1);
-      const unsigned row_off = (unsigned)(key * kstride) * 2u;
-      const unsigned dst = lds_wave + j * ROWS_PER_PASS * D * 2;  // this wave's 64 slots of the pass
-      lds_dma16(kgb, row_off + k_lane_off, dst + kb);
-      lds_dma16(vgb, row_off + v_lane_off, dst + vb);
+      for (int j = 0; j < PASSES; ++j) {
+        const unsigned dst = lds_wave + j * ROWS_PER_PASS * D * 2;  // this wave's 64 slots of the pass
+        lds_dma16(kgb + tile_off + j * pass_bytes, k_src, dst + kb);
+        lds_dma16(vgb + tile_off + j * pass_bytes, v_src, dst + vb);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PASSES; ++j) {
+        const int key = min(t * BT + j * ROWS_PER_PASS + slot_key, Lk - 1);
+        const unsigned row_off = (unsigned)(key * kstride) * 2u;
+        const unsigned dst = lds_wave + j * ROWS_PER_PASS * D * 2;
+        lds_dma16(kgb, row_off + k_lane_off, dst + kb);
+        lds_dma16(vgb, row_off + v_lane_off, dst + vb);
+      }
     }
   };
 
   // ---- per-lane LDS operand addresses (bytes; the block within a tile is an immediate).
   // K (A operand of S^T): row l32 (+32 per block), chunk 2*ks + half; the
-  // swizzle depends on row & 7 = l32 & 7 only.  k_addr points into the buffer of
+  // swizzle depends on (row >> 1) & 7 = (l32 >> 1) & 7 only.  k_addr points into the buffer of
   // the tile whose keys are read next.
   int k_addr[4];
 #pragma unroll
