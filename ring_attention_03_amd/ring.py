@@ -89,6 +89,10 @@ class RingAttention:
     epilogue (``attn_ring_step_merge``); with ``o_part``/``lse_part`` given and
     ``fused=False`` each step writes the partial buffers and
     ``attn_ring_merge`` folds them in.  Fully masked steps launch nothing.
+
+    ``prepare`` marshals every call of the ring once; the returned
+    ``PreparedRing`` can run the same ring on the same buffers many times with
+    no per-launch argument work (the schedule is static).
     """
 
     def __init__(self, layout: RingLayout, rank: int, scale: float = 0.0):
@@ -98,59 +102,89 @@ class RingAttention:
         self.rank = rank
         self.scale = scale
 
-    def run(self, q_local, kv_chunks, o_acc, lse_acc, o_part=None, lse_part=None, stream=None,
-            events=None, fused=True) -> int:
-        """Run the ring; returns the number of steps that launched work.
-
-        ``events``, if a list, receives ``(kind, start, end)`` timing events
-        (kind "step" or "merge") recorded on the launch stream around every
-        launch, for per-kernel timing.
-        """
+    def prepare(self, q_local, kv_chunks, o_acc, lse_acc, o_part=None, lse_part=None, stream=None,
+                fused=True) -> "PreparedRing":
         if not fused and (o_part is None or lse_part is None):
             raise ValueError("the unfused ring needs o_part and lse_part")
         lay, r = self.layout, self.rank
-        timed = _EventTimer(events, stream)
         cu = lay.cu
         q_pos0 = lay.pos0(r)
-        wrote_state = False
-        active = 0
+        steps = []
         for t in range(lay.n_chunks):
             j = ring_chunk(r, t, lay.n_chunks)
             k_j, v_j = kv_chunks[j]
             kw = dict(cu_q=cu, cu_k=cu, q_pos0=q_pos0, k_pos0=lay.pos0(j), scale=self.scale,
                       causal=True, stream=stream)
+            write = _native.prepare_ring_step(q_local, k_j, v_j, o_acc, lse_acc, report_skip=True, **kw)
+            if fused:
+                fold, merge = _native.prepare_ring_step_merge(q_local, k_j, v_j, o_acc, lse_acc, **kw), None
+            else:
+                fold = _native.prepare_ring_step(q_local, k_j, v_j, o_part, lse_part, report_skip=True, **kw)
+                merge = _native.prepare_ring_merge(o_acc, lse_acc, o_part, lse_part, stream=stream)
+            steps.append((write, fold, merge))
+        k_0, v_0 = kv_chunks[ring_chunk(r, 0, lay.n_chunks)]
+        identity = _native.prepare_ring_step(q_local, k_0, v_0, o_acc, lse_acc, cu_q=cu, cu_k=cu,
+                                             q_pos0=q_pos0, k_pos0=lay.pos0(r), scale=self.scale,
+                                             causal=True, report_skip=False, stream=stream)
+        return PreparedRing(steps, identity, stream)
+
+    def run(self, q_local, kv_chunks, o_acc, lse_acc, o_part=None, lse_part=None, stream=None,
+            events=None, fused=True) -> int:
+        """Run the ring once; returns the number of steps that launched work.
+
+        ``events``, if a list, receives ``(kind, start, end)`` timing events
+        (kind "step" or "merge") recorded on the launch stream around every
+        launch, for per-kernel timing.
+        """
+        ring = self.prepare(q_local, kv_chunks, o_acc, lse_acc, o_part, lse_part, stream, fused)
+        return ring.run(events=events)
+
+
+class PreparedRing:
+    """The calls of one ring, marshalled; ``run`` enqueues the whole ring."""
+
+    def __init__(self, steps, identity, stream):
+        self.steps, self.identity, self.stream = steps, identity, stream
+
+    def run(self, events=None, event_pool=None) -> int:
+        """Enqueue the ring; returns the number of steps that launched work.
+
+        ``events``/``event_pool`` as in ``RingAttention.run``; with a pool
+        (a list of timing-enabled events) the events are taken from it
+        instead of created per launch.
+        """
+        timed = _EventTimer(events, self.stream, event_pool)
+        wrote_state = False
+        active = 0
+        for write, fold, merge in self.steps:
             with timed("step") as mark:
-                if not wrote_state:
-                    launched = _native.attn_ring_step(q_local, k_j, v_j, o_acc, lse_acc,
-                                                      report_skip=True, **kw)
-                elif fused:
-                    launched = _native.attn_ring_step_merge(q_local, k_j, v_j, o_acc, lse_acc, **kw)
-                else:
-                    launched = _native.attn_ring_step(q_local, k_j, v_j, o_part, lse_part,
-                                                      report_skip=True, **kw)
+                launched = fold() if wrote_state else write()
                 mark(launched)
             if not launched:
                 continue
             active += 1
-            if wrote_state and not fused:
+            if wrote_state and merge is not None:
                 with timed("merge") as mark:
-                    _native.attn_ring_merge(o_acc, lse_acc, o_part, lse_part, stream=stream)
+                    merge()
                     mark(True)
             wrote_state = True
         if not wrote_state:  # every chunk was in the future: the state is the identity
-            k_j, v_j = kv_chunks[ring_chunk(r, 0, lay.n_chunks)]
-            _native.attn_ring_step(q_local, k_j, v_j, o_acc, lse_acc, cu_q=cu, cu_k=cu,
-                                   q_pos0=q_pos0, k_pos0=lay.pos0(r), scale=self.scale,
-                                   causal=True, report_skip=False, stream=stream)
+            self.identity()
         return active
 
 
 class _EventTimer:
     """Context manager factory recording HIP events around launches (no-op without a list)."""
 
-    def __init__(self, sink, stream):
+    def __init__(self, sink, stream, pool=None):
         self.sink = sink
         self.stream = stream
+        self.pool = pool
+
+    def event(self):
+        if self.pool:
+            return self.pool.pop()
+        return torch.cuda.Event(enable_timing=True)
 
     def __call__(self, kind):
         return _EventSpan(self, kind)
@@ -164,7 +198,7 @@ class _EventSpan:
 
     def __enter__(self):
         if self.timer.sink is not None:
-            self.start = torch.cuda.Event(enable_timing=True)
+            self.start = self.timer.event()
             self.start.record(self.timer.stream)
         return self._mark
 
@@ -173,7 +207,7 @@ class _EventSpan:
 
     def __exit__(self, *exc):
         if self.timer.sink is not None and self.keep and exc[0] is None:
-            end = torch.cuda.Event(enable_timing=True)
+            end = self.timer.event()
             end.record(self.timer.stream)
             self.timer.sink.append((self.kind, self.start, end))
         return False

@@ -61,25 +61,34 @@ def test_workload_recipe_is_seeded_and_shaped():
 
 
 class _FakeNative:
-    """Records the ring's library calls; a step "sees keys" when its chunk is not in the future."""
+    """Records the ring's library calls in launch order; a step "sees keys" when its chunk is not
+    in the future of the local rows."""
 
     def __init__(self, rank):
         self.rank = rank
         self.calls = []
 
-    def _visible(self, k_pos0, q_pos0):
+    @staticmethod
+    def _visible(k_pos0, q_pos0):
         return k_pos0[0] <= q_pos0[0]
 
-    def attn_ring_step(self, q, k, v, o, lse, *, q_pos0, k_pos0, report_skip=True, **kw):
-        self.calls.append(("step", o, k_pos0[0]))
-        return self._visible(k_pos0, q_pos0) or not report_skip
+    def prepare_ring_step(self, q, k, v, o, lse, *, q_pos0, k_pos0, report_skip=True, **kw):
+        def call():
+            self.calls.append(("step", o, k_pos0[0]))
+            return self._visible(k_pos0, q_pos0) or not report_skip
+        return call
 
-    def attn_ring_step_merge(self, q, k, v, o, lse, *, q_pos0, k_pos0, **kw):
-        self.calls.append(("step_merge", o, k_pos0[0]))
-        return self._visible(k_pos0, q_pos0)
+    def prepare_ring_step_merge(self, q, k, v, o, lse, *, q_pos0, k_pos0, **kw):
+        def call():
+            self.calls.append(("step_merge", o, k_pos0[0]))
+            return self._visible(k_pos0, q_pos0)
+        return call
 
-    def attn_ring_merge(self, o_acc, lse_acc, o_part, lse_part, **kw):
-        self.calls.append(("merge", o_acc, None))
+    def prepare_ring_merge(self, o_acc, lse_acc, o_part, lse_part, **kw):
+        def call():
+            self.calls.append(("merge", o_acc, None))
+            return True
+        return call
 
 
 @pytest.mark.parametrize("fused", [True, False])
