@@ -30,7 +30,7 @@ METRIC = "causal GQA prefill attention TFLOP/s & % bf16 peak at 32K/64K/100K, 1 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
 DOMINANT_KERNEL = "fwd_bf16_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16.json")
-KERNEL_SOURCES = ["fwd_bf16.hip", "kernels.h"]
+KERNEL_SOURCES = ["fwd_bf16.hip", "kernels.h", "merge_math.h"]
 
 
 def parse_args():
