@@ -39,7 +39,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="ring_64k_rank7")
-    ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,varlen_ulysses_rank7",
+    ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,varlen_ulysses_rank7,chunked_prefill_12k",
                     help="comma list of further workloads measured in the same run ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--extra-warmup", type=int, default=5)
@@ -71,7 +71,7 @@ class Job:
     def __init__(self, name, fused=True):
         import torch
 
-        from ring_attention_03_amd import RingAttention, RingLayout
+        from ring_attention_03_amd import ChunkedPrefill, RingAttention, RingLayout
         from ring_attention_03_amd.workloads import WORKLOADS, make_qkv
 
         self.w = w = WORKLOADS[name]
@@ -87,6 +87,10 @@ class Job:
             self.q = q.to(dev)
             self.k, self.v = k.to(dev), v.to(dev)
             self.cu = lay.cu
+        elif w.mode == "chunked":
+            self.q = lay.gather(q, self.rank).to(dev).contiguous()
+            self.k = lay.gather_prefix(k, self.rank).to(dev).contiguous()
+            self.v = lay.gather_prefix(v, self.rank).to(dev).contiguous()
         else:
             self.q = lay.gather(q, self.rank).to(dev).contiguous()
             self.chunks = [(lay.gather(k, j).to(dev).contiguous(), lay.gather(v, j).to(dev).contiguous())
@@ -106,12 +110,15 @@ class Job:
 
             self.prefill = lambda: attn_prefill_causal(self.q, self.k, self.v, self.o, self.lse,
                                                        cu_seqlens=self.cu)
+        elif w.mode == "chunked":
+            self.prefill = ChunkedPrefill(lay, self.rank).prepare(self.q, self.k, self.v, self.o,
+                                                                  self.lse)
         else:
             self.prepared = self.ring.prepare(self.q, self.chunks, self.o, self.lse, self.o_p,
                                               self.lse_p, fused=fused)
 
     def run(self, events=None, event_pool=None):
-        if self.w.n_chunks == 1:
+        if self.w.n_chunks == 1 or self.w.mode == "chunked":
             if events is None:
                 self.prefill()
             else:
@@ -124,11 +131,11 @@ class Job:
         return self.prepared.run(events=events, event_pool=event_pool)
 
     def launches_per_step(self):
-        return 1 if self.w.n_chunks == 1 else 2 * self.w.n_chunks
+        return 1 if self.w.n_chunks == 1 or self.w.mode == "chunked" else 2 * self.w.n_chunks
 
     def config(self):
         w = self.w
-        return {"workload": self.name, "seq_lens": list(w.seqlens), "ring_chunks": w.n_chunks,
+        return {"workload": self.name, "mode": w.mode, "seq_lens": list(w.seqlens), "ring_chunks": w.n_chunks,
                 "rank": self.rank, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                 "head_dim": w.head_dim, "causal": True, "local_q_rows": int(self.q.shape[0]),
                 "algorithmic_tflop": self.flops / 1e12,

@@ -64,6 +64,21 @@ class RingLayout:
         parts = [x[a:b] for a, b in self.ranges(chunk)]
         return parts[0] if len(parts) == 1 else torch.cat(parts, dim=0)
 
+    def prefix_cu(self, chunk: int):
+        """Prefix offsets of chunks 0..chunk of every sequence, packed (a chunked-prefill key set)."""
+        out = [0]
+        for c in self.chunk_lens:
+            out.append(out[-1] + (chunk + 1) * c)
+        return out
+
+    def gather_prefix(self, x: torch.Tensor, chunk: int) -> torch.Tensor:
+        """Chunks 0..chunk of every sequence of packed ``x``, packed (a view for one sequence)."""
+        parts, start = [], 0
+        for n, c in zip(self.seqlens, self.chunk_lens):
+            parts.append(x[start:start + (chunk + 1) * c])
+            start += n
+        return parts[0] if len(parts) == 1 else torch.cat(parts, dim=0)
+
     def visible_pairs(self, rank: int) -> int:
         """Causal (query, key) pairs whose query is in chunk ``rank``."""
         total = 0
@@ -138,6 +153,31 @@ class RingAttention:
         """
         ring = self.prepare(q_local, kv_chunks, o_acc, lse_acc, o_part, lse_part, stream, fused)
         return ring.run(events=events)
+
+
+class ChunkedPrefill:
+    """Chunked prefill of chunk ``index`` of every sequence: its queries attend
+    causally to the whole prefix (chunks 0..index) in one launch - full key
+    blocks plus a diagonal block, the same step kernel as the ring.  The result
+    is final (it equals full causal attention for those rows), so no merge is
+    needed.  SGLang's pipeline-parallel prefill runs prompts in such chunks
+    (chunked prefill size 12K in the pages' PP evaluation).
+    """
+
+    def __init__(self, layout: RingLayout, index: int, scale: float = 0.0):
+        if not 0 <= index < layout.n_chunks:
+            raise ValueError("chunk index outside the prompt")
+        self.layout, self.index, self.scale = layout, index, scale
+
+    def prepare(self, q_chunk, k_prefix, v_prefix, o, lse, stream=None):
+        lay = self.layout
+        return _native.prepare_ring_step(
+            q_chunk, k_prefix, v_prefix, o, lse, cu_q=lay.cu, cu_k=lay.prefix_cu(self.index),
+            q_pos0=lay.pos0(self.index), k_pos0=[0] * len(lay.seqlens), scale=self.scale,
+            causal=True, report_skip=False, stream=stream)
+
+    def run(self, q_chunk, k_prefix, v_prefix, o, lse, stream=None) -> None:
+        self.prepare(q_chunk, k_prefix, v_prefix, o, lse, stream)()
 
 
 class PreparedRing:

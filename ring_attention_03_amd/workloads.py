@@ -37,6 +37,10 @@ class Workload:
     dtype: str                # "bf16" or "fp32"
     v_dist: str = "normal"    # "normal" = N(0,1), "uniform" = U(-1,1)
     seed: int = 0
+    # "ring": the rank's query chunk against every key/value chunk in ring order;
+    # "chunked": chunked prefill - the rank's query chunk against its whole
+    # prefix (chunks 0..rank) in one call
+    mode: str = "ring"
     note: str = field(default="", compare=False)
 
     @property
@@ -64,9 +68,12 @@ WORKLOADS = {
     "ring_100k_n16": Workload(
         "ring_100k_n16", (102400,), 16, None, 64, 8, 64, "bf16", "normal", 4,
         "S=102400 in 16 ring chunks of 6400, every rank"),
+    "chunked_prefill_12k": Workload(
+        "chunked_prefill_12k", (98304,), 8, 7, 64, 8, 64, "bf16", "normal", 6, "chunked",
+        "chunked prefill: the 8th 12288-token chunk of a 98304-token prompt against its prefix"),
     "varlen_ulysses_rank7": Workload(
         "varlen_ulysses_rank7", (131072, 65536, 32768, 16384), 8, 7, 8, 1, 64, "bf16",
-        "normal", 5,
+        "normal", 5, "ring",
         "4 packed requests after a head all-to-all (8 q / 1 kv head), N=8, rank 7"),
 }
 

@@ -117,3 +117,22 @@ def test_unfused_ring_needs_partial_buffers():
     lay = RingLayout((32,), 4)
     with pytest.raises(ValueError):
         RingAttention(lay, 1).run("q", [("k", "v")] * 4, "acc", "lse", fused=False)
+
+
+@pytest.mark.parametrize("seqlens,n", [((512,), 4), ((300, 120, 60), 3)])
+def test_prefix_is_the_oracles_chunks_up_to_the_index(seqlens, n):
+    lay = RingLayout(seqlens, n)
+    x = torch.arange(sum(seqlens))
+    for i in range(n):
+        # per sequence: the rows of chunks 0..i, in order
+        want = []
+        cu = [0]
+        for b, (seq_len, c) in enumerate(zip(seqlens, lay.chunk_lens)):
+            seq_rows = []
+            for j in range(i + 1):
+                rows, ccu, _ = chunk_layout_ref(seqlens, n, j)
+                seq_rows += list(rows[ccu[b]:ccu[b + 1]])
+            want += seq_rows
+            cu.append(cu[-1] + len(seq_rows))
+        assert lay.gather_prefix(x, i).tolist() == want
+        assert lay.prefix_cu(i) == cu
