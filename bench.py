@@ -39,7 +39,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="ring_64k_rank7")
-    ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,varlen_ulysses_rank7,chunked_prefill_12k",
+    ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,varlen_ulysses_rank7,chunked_prefill_12k,"
+                    "ring_64k_zigzag_rank7",
                     help="comma list of further workloads measured in the same run ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--extra-warmup", type=int, default=5)
@@ -71,7 +72,8 @@ class Job:
     def __init__(self, name, fused=True):
         import torch
 
-        from ring_attention_03_amd import ChunkedPrefill, RingAttention, RingLayout
+        from ring_attention_03_amd import (ChunkedPrefill, RingAttention, RingLayout, ZigzagLayout,
+                                           ZigzagRing)
         from ring_attention_03_amd.workloads import WORKLOADS, make_qkv
 
         self.w = w = WORKLOADS[name]
@@ -87,6 +89,12 @@ class Job:
             self.q = q.to(dev)
             self.k, self.v = k.to(dev), v.to(dev)
             self.cu = lay.cu
+        elif w.mode == "zigzag":
+            zz = ZigzagLayout(w.seqlens, w.n_chunks)
+            self.q = zz.gather(q, self.rank).to(dev).contiguous()
+            self.chunks = [(zz.gather(k, j).to(dev).contiguous(), zz.gather(v, j).to(dev).contiguous())
+                           for j in range(w.n_chunks)]
+            self.zigzag = (zz, ZigzagRing(zz, self.rank))
         elif w.mode == "chunked":
             self.q = lay.gather(q, self.rank).to(dev).contiguous()
             self.k = lay.gather_prefix(k, self.rank).to(dev).contiguous()
@@ -100,9 +108,9 @@ class Job:
         self.o = torch.empty(tq, hq, d, device=dev)
         self.lse = torch.empty(hq, tq, device=dev)
         self.o_p = self.lse_p = None
-        if w.n_chunks > 1 and not fused:
+        if w.n_chunks > 1 and w.mode == "ring" and not fused:
             self.o_p, self.lse_p = torch.empty_like(self.o), torch.empty_like(self.lse)
-        self.pairs = lay.visible_pairs(self.rank)
+        self.pairs = (self.zigzag[0] if w.mode == "zigzag" else lay).visible_pairs(self.rank)
         self.flops = 4 * w.head_dim * w.num_q_heads * self.pairs
         # every launch's arguments are marshalled once: the timed loop only enqueues
         if w.n_chunks == 1:
@@ -113,6 +121,8 @@ class Job:
         elif w.mode == "chunked":
             self.prefill = ChunkedPrefill(lay, self.rank).prepare(self.q, self.k, self.v, self.o,
                                                                   self.lse)
+        elif w.mode == "zigzag":
+            self.prepared = self.zigzag[1].prepare(self.q, self.chunks, self.o, self.lse)
         else:
             self.prepared = self.ring.prepare(self.q, self.chunks, self.o, self.lse, self.o_p,
                                               self.lse_p, fused=fused)

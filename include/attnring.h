@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 #define ATTN_MAX_SEQS 64 /* packed sequences per call (their tables travel in kernel arguments) */
 
 typedef enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_FP32 = 1 } attn_dtype;
@@ -82,6 +82,12 @@ typedef struct {
   int32_t head_dim;       /* 64 */
   float scale;            /* > 0 and finite; 0 selects 1/sqrt(head_dim) */
   int32_t causal;         /* 1: mask keys whose position exceeds the query's; 0: no mask */
+  /* Optional explicit key ranges, instead of cu_k (which must then be NULL): sequence b's
+   * keys are rows k_row0[b] .. k_row0[b] + k_len[b] - 1 of k/v.  HOST [B] arrays, both or
+   * neither; ranges may overlap or come in any order (two query segments can attend to
+   * the same keys, as in load-balanced zigzag rings).  Not accepted by attn_prefill_causal. */
+  const int32_t* k_row0;
+  const int32_t* k_len;
 } attn_problem;
 
 /*

@@ -14,8 +14,9 @@ from ._native import (  # noqa: F401
     attn_ring_step_merge,
     load_library,
 )
-from .ring import ChunkedPrefill, RingAttention, RingLayout, ring_chunk  # noqa: F401
+from .ring import (ChunkedPrefill, RingAttention, RingLayout, ZigzagLayout, ZigzagRing,  # noqa: F401
+                   ring_chunk)
 
 __all__ = ["attn_ring_step", "attn_ring_step_merge", "attn_ring_merge", "attn_prefill_causal",
            "load_library", "AttnError", "RingAttention", "RingLayout", "ChunkedPrefill",
-           "ring_chunk"]
+           "ZigzagLayout", "ZigzagRing", "ring_chunk"]

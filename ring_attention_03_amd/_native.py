@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnring
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_DTYPE_BF16, ATTN_DTYPE_FP32 = 0, 1
 MAX_SEQS = 64
-ABI_VERSION = 2
+ABI_VERSION = 3
 EXPORTED = ("attn_ring_step", "attn_ring_step_merge", "attn_ring_merge", "attn_prefill_causal",
             "attn_last_error", "attn_abi_version")
 
@@ -43,6 +43,8 @@ class AttnProblem(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
+        ("k_row0", ctypes.POINTER(ctypes.c_int32)),
+        ("k_len", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -122,17 +124,18 @@ def _require_device(*tensors):
 
 
 def make_problem(q, k, *, cu_q=None, cu_k=None, q_pos0=None, k_pos0=None, scale=0.0,
-                 causal=True, num_seqs=None):
+                 causal=True, num_seqs=None, k_row0=None, k_len=None):
     """Build the C ``attn_problem`` for q [Tq, Hq, d] and k [Tk, Hkv, d]; returns (struct, keepalive)."""
     if num_seqs is None:
         num_seqs = 1 if cu_q is None else len(cu_q) - 1
     arrays = (_int_array(cu_q, num_seqs + 1), _int_array(cu_k, num_seqs + 1),
-              _int_array(q_pos0, num_seqs), _int_array(k_pos0, num_seqs))
+              _int_array(q_pos0, num_seqs), _int_array(k_pos0, num_seqs),
+              _int_array(k_row0, num_seqs), _int_array(k_len, num_seqs))
     as_ptr = [ctypes.cast(a, ctypes.POINTER(ctypes.c_int32)) if a is not None else None
               for a in arrays]
     prob = AttnProblem(num_seqs, as_ptr[0], as_ptr[1], as_ptr[2], as_ptr[3], q.shape[0],
                        k.shape[0], q.shape[1], k.shape[1], q.shape[2], float(scale),
-                       1 if causal else 0)
+                       1 if causal else 0, as_ptr[4], as_ptr[5])
     return prob, arrays
 
 
@@ -152,13 +155,13 @@ class PreparedCall:
 
 
 def _prepare_step(name, q, k, v, o, lse, *, cu_q, cu_k, q_pos0, k_pos0, scale, causal, report,
-                  stream):
+                  stream, k_row0=None, k_len=None):
     lib = load_library()
     _require_device(q, k, v, o, lse)
     _check_inputs(q, k, v)
     _check_out_shapes(q, o, lse)
     prob, keep = make_problem(q, k, cu_q=cu_q, cu_k=cu_k, q_pos0=q_pos0, k_pos0=k_pos0,
-                              scale=scale, causal=causal)
+                              scale=scale, causal=causal, k_row0=k_row0, k_len=k_len)
     launched = ctypes.c_int32(0) if report else None
     args = (ctypes.byref(prob), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
             ctypes.byref(launched) if report else None, _stream(stream))
@@ -166,19 +169,21 @@ def _prepare_step(name, q, k, v, o, lse, *, cu_q, cu_k, q_pos0, k_pos0, scale, c
 
 
 def prepare_ring_step(q, k, v, o_part, lse_part, *, cu_q=None, cu_k=None, q_pos0=None,
-                      k_pos0=None, scale=0.0, causal=True, report_skip=True, stream=None):
+                      k_pos0=None, scale=0.0, causal=True, report_skip=True, stream=None,
+                      k_row0=None, k_len=None):
     """``attn_ring_step`` with its arguments marshalled once (see ``attn_ring_step``)."""
     return _prepare_step("attn_ring_step", q, k, v, o_part, lse_part, cu_q=cu_q, cu_k=cu_k,
                          q_pos0=q_pos0, k_pos0=k_pos0, scale=scale, causal=causal,
-                         report=report_skip, stream=stream)
+                         report=report_skip, stream=stream, k_row0=k_row0, k_len=k_len)
 
 
 def prepare_ring_step_merge(q, k, v, o_acc, lse_acc, *, cu_q=None, cu_k=None, q_pos0=None,
-                            k_pos0=None, scale=0.0, causal=True, stream=None):
+                            k_pos0=None, scale=0.0, causal=True, stream=None, k_row0=None,
+                            k_len=None):
     """``attn_ring_step_merge`` with its arguments marshalled once."""
     return _prepare_step("attn_ring_step_merge", q, k, v, o_acc, lse_acc, cu_q=cu_q, cu_k=cu_k,
                          q_pos0=q_pos0, k_pos0=k_pos0, scale=scale, causal=causal, report=True,
-                         stream=stream)
+                         stream=stream, k_row0=k_row0, k_len=k_len)
 
 
 def prepare_ring_merge(o_acc, lse_acc, o_part, lse_part, *, stream=None):

@@ -56,12 +56,12 @@ attn_status check_offsets(const int32_t* cu, int32_t nseq, int32_t total, const 
   return ATTN_OK;
 }
 
-attn_status check_positions(const int32_t* pos, int32_t nseq, const int32_t* cu, const char* name,
+attn_status check_positions(const int32_t* pos, int32_t nseq, const int32_t* len, const char* name,
                             int32_t* out) {
   for (int b = 0; b < nseq; ++b) {
     const int64_t p0 = pos ? pos[b] : 0;
     if (p0 < 0) return fail(ATTN_EINVAL, "%s[%d]=%lld is negative", name, b, (long long)p0);
-    if (p0 + (cu[b + 1] - cu[b]) > INT32_MAX)
+    if (p0 + len[b] > INT32_MAX)
       return fail(ATTN_EINVAL, "%s[%d] + length overflows int32", name, b);
     out[b] = (int32_t)p0;
   }
@@ -97,18 +97,40 @@ attn_status plan_forward(const attn_problem* pr, attn_dtype dt, const void* q, c
     return fail(ATTN_EINVAL, "scale=%g must be finite and >= 0 (0 selects 1/sqrt(d))", (double)pr->scale);
   if (pr->causal != 0 && pr->causal != 1) return fail(ATTN_EINVAL, "causal=%d must be 0 or 1", pr->causal);
 
-  int32_t cq[ATTN_MAX_SEQS + 1], ck[ATTN_MAX_SEQS + 1], qp[ATTN_MAX_SEQS], kp[ATTN_MAX_SEQS];
+  int32_t cq[ATTN_MAX_SEQS + 1], ql[ATTN_MAX_SEQS], kr0[ATTN_MAX_SEQS], kl[ATTN_MAX_SEQS];
+  int32_t qp[ATTN_MAX_SEQS], kp[ATTN_MAX_SEQS];
   attn_status st;
   if ((st = check_offsets(pr->cu_q, nseq, pr->total_q, "cu_q", cq)) != ATTN_OK) return st;
-  if ((st = check_offsets(pr->cu_k, nseq, pr->total_k, "cu_k", ck)) != ATTN_OK) return st;
-  if ((st = check_positions(pr->q_pos0, nseq, cq, "q_pos0", qp)) != ATTN_OK) return st;
-  if ((st = check_positions(pr->k_pos0, nseq, ck, "k_pos0", kp)) != ATTN_OK) return st;
+  for (int b = 0; b < nseq; ++b) ql[b] = cq[b + 1] - cq[b];
+  if (pr->k_row0 || pr->k_len) {  // explicit key ranges: any order, may overlap
+    if (!pr->k_row0 || !pr->k_len) return fail(ATTN_EINVAL, "k_row0 and k_len must be given together");
+    if (pr->cu_k) return fail(ATTN_EINVAL, "give either cu_k or k_row0/k_len, not both");
+    for (int b = 0; b < nseq; ++b) {
+      if (pr->k_row0[b] < 0 || pr->k_len[b] < 0)
+        return fail(ATTN_EINVAL, "k_row0[%d]=%d / k_len[%d]=%d must be >= 0", b, pr->k_row0[b], b,
+                    pr->k_len[b]);
+      if ((int64_t)pr->k_row0[b] + pr->k_len[b] > pr->total_k)
+        return fail(ATTN_EINVAL, "keys of sequence %d end at row %lld, past total_k=%d", b,
+                    (long long)pr->k_row0[b] + pr->k_len[b], pr->total_k);
+      kr0[b] = pr->k_row0[b];
+      kl[b] = pr->k_len[b];
+    }
+  } else {
+    int32_t ck[ATTN_MAX_SEQS + 1];
+    if ((st = check_offsets(pr->cu_k, nseq, pr->total_k, "cu_k", ck)) != ATTN_OK) return st;
+    for (int b = 0; b < nseq; ++b) {
+      kr0[b] = ck[b];
+      kl[b] = ck[b + 1] - ck[b];
+    }
+  }
+  if ((st = check_positions(pr->q_pos0, nseq, ql, "q_pos0", qp)) != ATTN_OK) return st;
+  if ((st = check_positions(pr->k_pos0, nseq, kl, "k_pos0", kp)) != ATTN_OK) return st;
 
   const size_t esz = dt == ATTN_DTYPE_BF16 ? 2 : 4;
   const int64_t d = pr->head_dim;
   // the bf16 kernel addresses one sequence's keys and values with 32-bit byte offsets
   for (int b = 0; b < nseq && dt == ATTN_DTYPE_BF16; ++b)
-    if ((int64_t)(ck[b + 1] - ck[b]) * pr->num_kv_heads * d * 2 >= (int64_t(1) << 31))
+    if ((int64_t)kl[b] * pr->num_kv_heads * d * 2 >= (int64_t(1) << 31))
       return fail(ATTN_EUNSUPPORTED, "sequence %d: keys and values span 2 GiB or more per tensor", b);
   const size_t q_bytes = (size_t)pr->total_q * pr->num_q_heads * d * esz;
   const size_t kv_bytes = (size_t)pr->total_k * pr->num_kv_heads * d * esz;
@@ -156,7 +178,7 @@ attn_status plan_forward(const attn_problem* pr, attn_dtype dt, const void* q, c
   int order[ATTN_MAX_SEQS];
   double work[ATTN_MAX_SEQS];
   for (int b = 0; b < nseq; ++b) {
-    const int64_t lq = cq[b + 1] - cq[b], lk = ck[b + 1] - ck[b];
+    const int64_t lq = ql[b], lk = kl[b];
     int64_t kend = lk;
     if (pr->causal) kend = std::min<int64_t>(lk, std::max<int64_t>(0, (int64_t)qp[b] + lq - 1 - kp[b] + 1));
     if (lq > 0 && kend > 0) any_visible = true;
@@ -170,8 +192,8 @@ attn_status plan_forward(const attn_problem* pr, attn_dtype dt, const void* q, c
     const int b = order[i];
     p.q_row0[i] = cq[b];
     p.q_len[i] = cq[b + 1] - cq[b];
-    p.k_row0[i] = ck[b];
-    p.k_len[i] = ck[b + 1] - ck[b];
+    p.k_row0[i] = kr0[b];
+    p.k_len[i] = kl[b];
     p.q_pos0[i] = qp[b];
     p.k_pos0[i] = kp[b];
     p.unit_off[i] = units;
@@ -244,6 +266,8 @@ attn_status attn_prefill_causal(const attn_problem* problem, attn_dtype dtype, c
     return fail(ATTN_EINVAL, "prefill needs cu_k equal to cu_q");
   if ((problem->q_pos0 == nullptr) != (problem->k_pos0 == nullptr))
     return fail(ATTN_EINVAL, "prefill needs k_pos0 equal to q_pos0");
+  if (problem->k_row0 || problem->k_len)
+    return fail(ATTN_EINVAL, "prefill takes its keys from cu_k (k_row0/k_len must be NULL)");
   const int32_t nseq = problem->num_seqs;
   if (nseq >= 1 && nseq <= ATTN_MAX_SEQS) {
     if (problem->cu_q)

@@ -155,6 +155,128 @@ class RingAttention:
         return ring.run(events=events)
 
 
+class ZigzagLayout:
+    """Load-balanced causal ring: every sequence is cut into 2N equal chunks and
+    device r holds chunks r and 2N-1-r (an early and a late one), so every
+    device does the same causal work, where contiguous chunks give device N-1
+    N times the work of device 0.  The kernels take arbitrary per-sequence
+    positions and key ranges, so only the host schedule differs from the
+    contiguous ring.  A device's local rows (and the key/value pair it holds)
+    are packed per sequence as [early chunk; late chunk].
+    """
+
+    def __init__(self, seqlens, n_devices: int):
+        self.seqlens = tuple(seqlens)
+        self.n = n_devices
+        self.chunks = RingLayout(self.seqlens, 2 * n_devices)
+
+    @property
+    def chunk_lens(self):
+        return self.chunks.chunk_lens
+
+    def pair(self, dev: int):
+        return dev, 2 * self.n - 1 - dev
+
+    def cu(self):
+        """Packed offsets of the 2B segments (early, late per sequence) of a local pair."""
+        out = [0]
+        for c in self.chunk_lens:
+            out += [out[-1] + c, out[-1] + 2 * c]
+        return out
+
+    def positions(self, dev: int):
+        """Global position of each segment's first token on device ``dev``."""
+        lo, hi = self.pair(dev)
+        out = []
+        for c in self.chunk_lens:
+            out += [lo * c, hi * c]
+        return out
+
+    def gather(self, x: torch.Tensor, dev: int) -> torch.Tensor:
+        """Device ``dev``'s rows of packed ``x``: per sequence its early then late chunk."""
+        lo, hi = self.pair(dev)
+        parts = []
+        for (a, b), (c, d) in zip(self.chunks.ranges(lo), self.chunks.ranges(hi)):
+            parts += [x[a:b], x[c:d]]
+        return torch.cat(parts, dim=0)
+
+    def visible_pairs(self, dev: int) -> int:
+        lo, hi = self.pair(dev)
+        return self.chunks.visible_pairs(lo) + self.chunks.visible_pairs(hi)
+
+
+class ZigzagRing:
+    """Device ``rank``'s share of a zigzag ring (see ZigzagLayout).
+
+    At step t the device holds device j = (rank - t) mod N's key/value pair
+    (X = chunk j, Y = chunk 2N-1-j) and its own query pair (A = chunk rank,
+    B = chunk 2N-1-rank).  A sees X only when j <= rank and never Y; B always
+    sees all of X and sees Y when j >= rank.  Each step is two launches over
+    the 2B packed query segments, each segment once per launch: {A-X, B-Y}
+    and {B-X} (A given no keys).  The first launch (the diagonal pair, j =
+    rank) writes the running state; every other launch merges into it, and a
+    launch whose keys are all in the future enqueues nothing.
+    """
+
+    def __init__(self, layout: ZigzagLayout, rank: int, scale: float = 0.0):
+        if not 0 <= rank < layout.n:
+            raise ValueError("rank outside the ring")
+        self.layout, self.rank, self.scale = layout, rank, scale
+
+    def prepare(self, q_local, kv_pairs, o, lse, stream=None) -> "PreparedRing":
+        lay, r = self.layout, self.rank
+        cu = lay.cu()
+        q_pos0 = lay.positions(r)
+        nb = len(lay.seqlens)
+        calls = []
+        for t in range(lay.n):
+            j = (r - t) % lay.n
+            k_j, v_j = kv_pairs[j]
+            kpos = lay.positions(j)
+            x_row0 = [cu[2 * b] for b in range(nb)]
+            y_row0 = [cu[2 * b + 1] for b in range(nb)]
+            c = lay.chunk_lens
+            launches = [
+                # {A-X, B-Y}
+                dict(k_row0=[v for b in range(nb) for v in (x_row0[b], y_row0[b])],
+                     k_len=[v for b in range(nb) for v in (c[b], c[b])],
+                     k_pos0=[v for b in range(nb) for v in (kpos[2 * b], kpos[2 * b + 1])]),
+                # {B-X}; A gets no keys
+                dict(k_row0=[v for b in range(nb) for v in (x_row0[b], x_row0[b])],
+                     k_len=[v for b in range(nb) for v in (0, c[b])],
+                     k_pos0=[v for b in range(nb) for v in (kpos[2 * b], kpos[2 * b])]),
+            ]
+            for li, kw in enumerate(launches):
+                args = dict(cu_q=cu, q_pos0=q_pos0, scale=self.scale, causal=True, stream=stream, **kw)
+                if t == 0 and li == 0:
+                    calls.append(_native.prepare_ring_step(q_local, k_j, v_j, o, lse,
+                                                           report_skip=False, **args))
+                else:
+                    calls.append(_native.prepare_ring_step_merge(q_local, k_j, v_j, o, lse, **args))
+        return PreparedCalls(calls, stream)
+
+    def run(self, q_local, kv_pairs, o, lse, stream=None, events=None) -> int:
+        return self.prepare(q_local, kv_pairs, o, lse, stream).run(events=events)
+
+
+class PreparedCalls:
+    """A fixed sequence of prepared launches; ``run`` enqueues them in order and
+    returns how many launched (a fully masked merge launches nothing)."""
+
+    def __init__(self, calls, stream):
+        self.calls, self.stream = calls, stream
+
+    def run(self, events=None, event_pool=None) -> int:
+        timed = _EventTimer(events, self.stream, event_pool)
+        active = 0
+        for call in self.calls:
+            with timed("step") as mark:
+                launched = call()
+                mark(launched)
+            active += bool(launched)
+        return active
+
+
 class ChunkedPrefill:
     """Chunked prefill of chunk ``index`` of every sequence: its queries attend
     causally to the whole prefix (chunks 0..index) in one launch - full key

@@ -39,7 +39,9 @@ class Workload:
     seed: int = 0
     # "ring": the rank's query chunk against every key/value chunk in ring order;
     # "chunked": chunked prefill - the rank's query chunk against its whole
-    # prefix (chunks 0..rank) in one call
+    # prefix (chunks 0..rank) in one call;
+    # "zigzag": load-balanced ring - sequences cut into 2N chunks, device r
+    # holds chunks r and 2N-1-r (n_chunks is the device count N)
     mode: str = "ring"
     note: str = field(default="", compare=False)
 
@@ -68,6 +70,9 @@ WORKLOADS = {
     "ring_100k_n16": Workload(
         "ring_100k_n16", (102400,), 16, None, 64, 8, 64, "bf16", "normal", 4,
         "S=102400 in 16 ring chunks of 6400, every rank"),
+    "ring_64k_zigzag_rank7": Workload(
+        "ring_64k_zigzag_rank7", (65536,), 8, 7, 64, 8, 64, "bf16", "uniform", 3, "zigzag",
+        "S=65536 on 8 devices, load-balanced: 16 chunks of 4096, rank 7 holds chunks 7 and 8"),
     "chunked_prefill_12k": Workload(
         "chunked_prefill_12k", (98304,), 8, 7, 64, 8, 64, "bf16", "normal", 6, "chunked",
         "chunked prefill: the 8th 12288-token chunk of a 98304-token prompt against its prefix"),

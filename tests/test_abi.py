@@ -37,14 +37,16 @@ def test_library_exports_every_declared_symbol():
     lib = _native.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == _native.ABI_VERSION == 2
+    assert lib.attn_abi_version() == _native.ABI_VERSION == 3
     assert lib.attn_last_error() is not None
 
 
 def test_problem_struct_layout_matches_header():
-    # 5 pointers after an int32 (padded), 7 int32/float fields: checks ctypes mirrors the C struct
-    assert ctypes.sizeof(_native.AttnProblem) == 8 + 4 * 8 + 7 * 4 + 4
+    # 4 pointers after an int32 (padded), 7 int32/float fields (padded), 2 pointers: checks
+    # ctypes mirrors the C struct
+    assert ctypes.sizeof(_native.AttnProblem) == 8 + 4 * 8 + 7 * 4 + 4 + 2 * 8
     assert _native.AttnProblem.total_q.offset == 40
+    assert _native.AttnProblem.k_row0.offset == 72 and _native.AttnProblem.k_len.offset == 80
 
 
 FAKE = 1 << 32  # 16-byte aligned placeholder address, never dereferenced on the host
@@ -58,7 +60,7 @@ def _prob(**kw):
     arrays = {}
     p = _native.AttnProblem()
     for key, val in base.items():
-        if key in ("cu_q", "cu_k", "q_pos0", "k_pos0"):
+        if key in ("cu_q", "cu_k", "q_pos0", "k_pos0", "k_row0", "k_len"):
             arr = (ctypes.c_int32 * len(val))(*val)
             arrays[key] = arr
             setattr(p, key, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
@@ -96,6 +98,14 @@ def _step(p, dtype=0, ptrs=None, launched=True):
     (dict(k_pos0=[2**31 - 10]), 1, "overflow"),
     # bf16 keys of one sequence: 2**21 rows x 8 heads x 64 x 2 B = 2 GiB
     (dict(total_k=2**21, num_q_heads=8, num_kv_heads=8, causal=0), 2, "2 GiB"),
+    # explicit key ranges
+    (dict(k_row0=[0]), 1, "together"),
+    (dict(k_len=[10]), 1, "together"),
+    (dict(k_row0=[0], k_len=[10], cu_k=[0, 128]), 1, "not both"),
+    (dict(k_row0=[-1], k_len=[10]), 1, ">= 0"),
+    (dict(k_row0=[100], k_len=[29]), 1, "past total_k"),
+    (dict(num_seqs=2, cu_q=[0, 64, 128], k_row0=[0, 0], k_len=[128, 129]), 1, "past total_k"),
+    (dict(k_row0=[0], k_len=[10], k_pos0=[2**31 - 5]), 1, "overflow"),
 ])
 def test_invalid_problem_is_rejected_before_launch(kw, expect, needle):
     p, keep = _prob(**kw)
@@ -103,6 +113,22 @@ def test_invalid_problem_is_rejected_before_launch(kw, expect, needle):
     assert st == expect, msg
     assert needle in msg
     assert launched == 0
+    del keep
+
+
+@no_gpu_only
+def test_explicit_key_ranges_may_overlap_and_prefill_refuses_them():
+    # two query sequences attending to the same 64 keys (overlapping ranges) is valid:
+    # with every key in the future of every query nothing is enqueued (no GPU needed)
+    p, keep = _prob(num_seqs=2, cu_q=[0, 64, 128], k_row0=[0, 0], k_len=[64, 64],
+                    q_pos0=[0, 64], k_pos0=[500, 500])
+    st, launched, msg = _step(p)
+    assert st == 0 and launched == 0, msg
+    lib = _native.load_library()
+    p, keep = _prob(k_row0=[0], k_len=[128])
+    assert lib.attn_prefill_causal(ctypes.byref(p), 0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4,
+                                   FAKE * 5, None) == 1
+    assert "k_row0" in lib.attn_last_error().decode()
     del keep
 
 

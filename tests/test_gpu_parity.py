@@ -19,8 +19,8 @@ import torch
 
 from oracle import attention_ref, causal_attention_ref, chunk_layout_ref, merge_ref, ring_ref
 from ring_attention_03_amd import (AttnError, ChunkedPrefill, RingAttention, RingLayout,
-                                   attn_prefill_causal, attn_ring_merge, attn_ring_step,
-                                   attn_ring_step_merge)
+                                   ZigzagLayout, ZigzagRing, attn_prefill_causal, attn_ring_merge,
+                                   attn_ring_step, attn_ring_step_merge)
 from ring_attention_03_amd.workloads import WORKLOADS, make_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -136,6 +136,58 @@ def test_chunked_prefill_every_chunk(seqlens, n, hq, hkv, dtype):
         rows, _, _ = chunk_layout_ref(seqlens, n, i)
         o_ref, lse_ref = causal_attention_ref(q, k, v, seqlens, rows=rows)
         assert_close(o, lse, o_ref, lse_ref, *tol, f"chunk {i}")
+
+
+def run_zigzag(q, k, v, seqlens, n, rank):
+    """Device ``rank``'s zigzag ring on the GPU from full packed CPU tensors; CPU (O, LSE)."""
+    zz = ZigzagLayout(tuple(seqlens), n)
+    dev = "cuda"
+    q_local = zz.gather(q, rank).to(dev).contiguous()
+    pairs = [(zz.gather(k, j).to(dev).contiguous(), zz.gather(v, j).to(dev).contiguous())
+             for j in range(n)]
+    tq, hq, d = q_local.shape
+    o = torch.full((tq, hq, d), float("nan"), device=dev)  # every row must be written
+    lse = torch.full((hq, tq), float("nan"), device=dev)
+    ZigzagRing(zz, rank).run(q_local, pairs, o, lse)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def zigzag_rows(seqlens, n, rank):
+    """Global packed rows of device ``rank`` in its packed order (per sequence: early, late chunk)."""
+    lo, _, _ = chunk_layout_ref(seqlens, 2 * n, rank)
+    hi, _, _ = chunk_layout_ref(seqlens, 2 * n, 2 * n - 1 - rank)
+    c = [s // (2 * n) for s in seqlens]
+    rows, a = [], 0
+    for cb in c:
+        rows += list(lo[a:a + cb]) + list(hi[a:a + cb])
+        a += cb
+    return rows
+
+
+ZIGZAG_CASES = [
+    # (seqlens, N devices, Hq, Hkv, dtype)
+    ((2048,), 4, 16, 2, "bf16"),                 # 8 chunks of 256
+    ((1000, 600), 2, 8, 1, "bf16"),              # varlen, ragged chunks (250, 150)
+    ((256,), 2, 4, 1, "fp32"),                   # the fp32 path
+]
+
+
+@pytest.mark.parametrize("seqlens,n,hq,hkv,dtype", ZIGZAG_CASES)
+def test_zigzag_ring_every_rank(seqlens, n, hq, hkv, dtype):
+    # each device's two chunks after its zigzag ring equal full causal attention
+    # for those rows, and every device does the same causal work
+    w = WORKLOADS["ring_64k_zigzag_rank7"].scaled(seqlens=seqlens, n_chunks=n, num_q_heads=hq,
+                                                  num_kv_heads=hkv, dtype=dtype, seed=24)
+    q, k, v = make_qkv(w)
+    tol = (O_TOL_BF16, LSE_TOL_BF16) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    pairs = [ZigzagLayout(seqlens, n).visible_pairs(r) for r in range(n)]
+    assert len(set(pairs)) == 1
+    for r in range(n):
+        log(f"zigzag ring {seqlens} N={n} rank {r} {dtype}")
+        o, lse = run_zigzag(q, k, v, seqlens, n, r)
+        o_ref, lse_ref = causal_attention_ref(q, k, v, seqlens, rows=zigzag_rows(seqlens, n, r))
+        assert_close(o, lse, o_ref, lse_ref, *tol, f"zigzag rank {r}")
 
 
 def _prefill(q, k, v, seqlens=None):
@@ -396,6 +448,20 @@ def test_full_size_chunked_prefill_sampled_rows():
     log(f"full-size chunked_prefill_12k: oracle on {len(local)} rows")
     o_ref, lse_ref = causal_attention_ref(q, k, v, w.seqlens, rows=[rows[r] for r in local])
     assert_close(o[local], lse[:, local], o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, "chunked 12k")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_full_size_zigzag_sampled_rows(rank):
+    w = WORKLOADS["ring_64k_zigzag_rank7"]
+    log(f"full-size zigzag rank {rank}: generating inputs")
+    q, k, v = make_qkv(w)
+    o, lse = run_zigzag(q, k, v, w.seqlens, w.n_chunks, rank)
+    local = sample_rows(o.shape[0], 24, w.seed + rank)
+    rows = zigzag_rows(w.seqlens, w.n_chunks, rank)
+    log(f"full-size zigzag rank {rank}: oracle on {len(local)} rows")
+    o_ref, lse_ref = causal_attention_ref(q, k, v, w.seqlens, rows=[rows[r] for r in local])
+    assert_close(o[local], lse[:, local], o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, "zigzag 64k")
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 

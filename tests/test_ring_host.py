@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from oracle import chunk_layout_ref, visible_pairs_ref
-from ring_attention_03_amd.ring import RingAttention, RingLayout, ring_chunk
+from ring_attention_03_amd.ring import RingAttention, RingLayout, ZigzagLayout, ring_chunk
 from ring_attention_03_amd.workloads import WORKLOADS, make_qkv, sample_rows
 
 
@@ -136,3 +136,22 @@ def test_prefix_is_the_oracles_chunks_up_to_the_index(seqlens, n):
             cu.append(cu[-1] + len(seq_rows))
         assert lay.gather_prefix(x, i).tolist() == want
         assert lay.prefix_cu(i) == cu
+
+
+@pytest.mark.parametrize("seqlens,n", [((64,), 4), ((40, 24), 2)])
+def test_zigzag_layout_matches_oracle_chunks_and_balances_work(seqlens, n):
+    zz = ZigzagLayout(seqlens, n)
+    x = torch.arange(sum(seqlens))
+    for r in range(n):
+        lo, lo_cu, lo_pos = chunk_layout_ref(seqlens, 2 * n, r)
+        hi, hi_cu, hi_pos = chunk_layout_ref(seqlens, 2 * n, 2 * n - 1 - r)
+        want, pos = [], []
+        for b in range(len(seqlens)):
+            want += list(lo[lo_cu[b]:lo_cu[b + 1]]) + list(hi[hi_cu[b]:hi_cu[b + 1]])
+            pos += [lo_pos[b], hi_pos[b]]
+        assert zz.gather(x, r).tolist() == want
+        assert zz.positions(r) == pos
+        # causal pairs of the device's rows, counted directly
+        assert zz.visible_pairs(r) == (visible_pairs_ref(seqlens, 2 * n, r)
+                                       + visible_pairs_ref(seqlens, 2 * n, 2 * n - 1 - r))
+    assert len({zz.visible_pairs(r) for r in range(n)}) == 1
