@@ -55,6 +55,12 @@ def parse_args():
                     help="only derive HBM bytes per attention launch from four rocprofv3 --pmc output "
                          "folders (FETCH_SIZE and WRITE_SIZE of a bench run, then of --calibrate-copy) "
                          "and write them to " + os.path.relpath(TRAFFIC_FILE, ROOT))
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only measure the sustained rate of a large library bf16 GEMM on random data "
+                         "(the practical matrix-core ceiling under the board's power limit)")
+    ap.add_argument("--counters-from", metavar="FOLDER",
+                    help="only summarize a rocprofv3 --pmc --kernel-trace run of this script "
+                         "(MFMA busy, LDS bank conflicts, shader clock) for the attention kernel")
     return ap.parse_args()
 
 
@@ -310,8 +316,89 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload
     print(json.dumps(rec), flush=True)
 
 
+# MI355X: 256 compute units of 4 SIMDs in 8 accelerator complex dies (XCDs)
+N_CU, N_XCD, SIMD_PER_CU = 256, 8, 4
+
+
+def summarize_counters(folder):
+    """Derived figures of the attention kernel from one rocprofv3 --pmc --kernel-trace run.
+
+    Counter values are summed over their hardware instances per dispatch, then
+    averaged over the kernel's dispatches.  GRBM_GUI_ACTIVE counts busy clocks
+    of every XCD, so one XCD's share over the traced duration gives the
+    shader clock; SQ_VALU_MFMA_BUSY_CYCLES counts per SIMD, so dividing by
+    that clock count times the SIMD count gives the matrix cores' busy
+    fraction at the clock the kernel actually ran.
+    """
+    import csv
+    import glob
+
+    names = ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+             "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAVES", "SQ_BUSY_CYCLES"]
+    vals = {n: _counter_per_dispatch(folder, n, DOMINANT_KERNEL)[0] for n in names}
+    durs = []
+    for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if DOMINANT_KERNEL in r["Kernel_Name"]:
+                    durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    if not durs:
+        raise SystemExit(f"no kernel trace of {DOMINANT_KERNEL} under {folder}")
+    dur = sum(durs) / len(durs)
+    clocks = vals["GRBM_GUI_ACTIVE"] / N_XCD
+    simds = N_CU * SIMD_PER_CU
+    mfma_busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (clocks * simds)
+    rec = {"kernel": DOMINANT_KERNEL, "kernel_source_sha": kernel_source_hash(), "dispatches": len(durs),
+           "avg_duration_us": dur * 1e6, "shader_clock_ghz": clocks / dur / 1e9,
+           "mfma_busy_pct": 100.0 * mfma_busy,
+           "mfma_instructions": vals["SQ_INSTS_MFMA"],
+           "valu_per_mfma": vals["SQ_INSTS_VALU"] / vals["SQ_INSTS_MFMA"],
+           "lds_per_mfma": vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"],
+           "lds_bank_conflict_pct": 100.0 * vals["SQ_LDS_BANK_CONFLICT"] / max(vals["SQ_LDS_IDX_ACTIVE"], 1.0),
+           "lds_active_pct": 100.0 * vals["SQ_LDS_IDX_ACTIVE"] / (clocks * N_CU),
+           "waves": vals["SQ_WAVES"],
+           "raw": vals}
+    print(json.dumps(rec, indent=1), flush=True)
+
+
+def gemm_ceiling():
+    """Sustained bf16 GEMM rate of the vendor library on N(0,1) data.
+
+    The published dense peak assumes the top shader clock; with random
+    operands the matrix cores draw enough power that the board lowers its
+    clock, so a large library GEMM measures the rate that is reachable in
+    practice.  The GPU is kept busy for a few seconds first so the clock
+    has settled.
+    """
+    import torch
+
+    n = 8192
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 3.0:
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    reps = 50
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"gemm": f"bf16 {n}x{n}x{n}, N(0,1) operands, torch.matmul (vendor BLAS)",
+                      "ms": ms, "tflops": tf, "pct_bf16_peak": 100.0 * tf / PEAK_BF16_TFLOPS}), flush=True)
+
+
 def main():
     args = parse_args()
+    if args.counters_from:
+        summarize_counters(args.counters_from)
+        return
     if args.traffic_from:
         write_traffic(*args.traffic_from, workload=args.workload, copy_mib=args.calibrate_copy or 2048)
         return
@@ -326,6 +413,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling()
         return
     from ring_attention_03_amd import load_library
 
