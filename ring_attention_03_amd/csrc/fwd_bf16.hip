@@ -22,9 +22,10 @@
 // and S = K Q^T of block i+1 (matrix cores), which do not depend on it, so a
 // single wave keeps both units busy and the other resident waves fill the
 // gaps.  Keys of block i are read from LDS one step before its softmax and
-// values one step after, so values live one tile longer than keys: LDS holds
-// two key buffers and three value buffers (80 KiB), and one barrier per tile
-// separates the copy of tile t+2 from the last reads of the buffers it reuses.
+// values at the end of it (held in registers for the next step's O += P V),
+// so values live one tile longer than keys: LDS holds two key buffers and
+// three value buffers (80 KiB), and one barrier per tile separates the copy of
+// tile t+2 from the last reads of the buffers it reuses.
 //
 // Register layouts (v_mfma_f32_32x32x16_bf16: A is 32x16, B is 16x32, lane l
 // supplies row/col l%32 and k-slots 8*(l/32)..+7; D lane l holds column l%32,
@@ -277,6 +278,7 @@ void fwd_bf16_kernel(FwdParams p) {
   asm volatile("" ::"s"(c2));
   f32x16 S[2];              // scores of blocks i (S[i&1]) and i+1: keys x this wave's 32 queries
   bf16x8 P[2][2];           // bf16 probabilities of blocks i and i-1 ([i&1]), per 16-key step
+  bf16x8 vnext[4];          // values of the block whose O += P V comes next
 
   // K operand of 16-key step ks of block `sub` in the current key buffer
   auto kread = [&](int ks, auto sub_tag) __attribute__((always_inline)) {
@@ -343,7 +345,9 @@ void fwd_bf16_kernel(FwdParams p) {
   // registers), the reference is raised to the row max with acc and l
   // rescaled, and the exponentials redone.
   //
-  // Buffers: block i's keys are read at step i-1 and its values at step i+1.
+  // Buffers: block i's keys are read at step i-1 and its values at the end of
+  // step i, after the matrix work is issued, so their latency is covered by
+  // the step's tail and they are in registers when step i+1 starts.
   // At J == 3, between the two halves, all waves meet at the tile barrier: by
   // then every wave has read the keys of this tile and the values of the tile
   // before it, so the next-but-one tile is copied into those buffers.  The
@@ -354,17 +358,11 @@ void fwd_bf16_kernel(FwdParams p) {
     constexpr int CUR = J & 1, NXT = CUR ^ 1;
     const bool masked = i >= nfull;  // workgroup-uniform
     if (masked) mask(S[CUR], i);
-    if constexpr (J == 1) advance_v(i >> 2);
+    if constexpr (J == 0) advance_v(i >> 2);
     float part[4];
     // ---- first half: exponentials of keys 0..15 with O += V^T P^T of block i-1
     {
-      bf16x8 va[4];
-      {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int db = 0; db < 2; ++db) va[2 * st + db] = vread(st, db, Int<(J + 3) & 3>{});
-      }
+      const bf16x8* va = vnext;
       exps_half(S[CUR], P[CUR][0], part, Int<0>{});
       {
 #pragma unroll
@@ -372,7 +370,6 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
           for (int db = 0; db < 2; ++db)
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[2 * st + db], P[NXT][st], acc[db], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // value reads
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // exp / fma / add / convert
@@ -412,6 +409,15 @@ void fwd_bf16_kernel(FwdParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    // values of this block for the next step's O += P V (its tile was published
+    // at the previous tile's barrier and is overwritten two barriers later)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) vnext[2 * st + db] = vread(st, db, Int<J>{});
+    // convert the probabilities here, before the check, so the conversions sit
+    // among this step's instructions instead of trailing it
+    asm volatile("" ::"v"(P[CUR][0]), "v"(P[CUR][1]));
     float rs = (part[0] + part[1]) + (part[2] + part[3]);
     if (__builtin_amdgcn_ballot_w64(rs > SUM_LIMIT) != 0) {  // wave-uniform, rare
       f32x16& Sb = S[CUR];
@@ -450,6 +456,8 @@ void fwd_bf16_kernel(FwdParams p) {
   // the end from whatever the key buffer holds; both results are unused.
   P[1][0] = bf16x8{};
   P[1][1] = bf16x8{};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) vnext[k] = bf16x8{};
   if (nblk > 0) {
     copy_tile(0);
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the queries and this wave's share of tile 0
@@ -460,15 +468,15 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int ks = 0; ks < 4; ++ks)
       S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<0>{}), qr[ks], S[0], 0, 0, 0);
   }
-  // O += V^T P^T of the last block (its step J did not advance the value buffer if J == 0)
+  // O += V^T P^T of the last block (its values were read at the end of its step)
   auto last_pv = [&](auto j_tag, int i) __attribute__((always_inline)) {
     constexpr int J = decltype(j_tag)::value;
-    if constexpr (J == 0) advance_v(i >> 2);
+    (void)i;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int db = 0; db < 2; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(st, db, Int<J>{}), P[J & 1][st], acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vnext[2 * st + db], P[J & 1][st], acc[db], 0, 0, 0);
   };
   if (nblk > 0) {
     for (int i0 = 0; i0 < nblk; i0 += 4) {
@@ -485,10 +493,14 @@ void fwd_bf16_kernel(FwdParams p) {
   // leave the state as it is)
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int row = rw0 + l32;
+  // (the lane index is taken afresh from the exec mask, so no lane-derived value
+  // has to stay live across the loop)
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int half_e = lane_e >> 5;
+  const int row = rw0 + (lane_e & 31);
   if (row < Lq) {
     const size_t grow = (size_t)(p.q_row0[s] + row);
-    float* dst = p.o + (grow * p.hq + head) * D + half * 4;
+    float* dst = p.o + (grow * p.hq + head) * D + half_e * 4;
     float* lse_dst = p.lse + (size_t)head * p.total_q + grow;
     const float lse_b = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
     if (!p.merge) {
@@ -503,7 +515,7 @@ void fwd_bf16_kernel(FwdParams p) {
           v4[3] = acc[db][i * 4 + 3] * inv;
           *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = v4;
         }
-      if (half == 0) *lse_dst = lse_b;
+      if (half_e == 0) *lse_dst = lse_b;
     } else if (l_tot > 0.f) {
       float lse, wa, wb;
       lse_merge_weights(*lse_dst, lse_b, &lse, &wa, &wb);  // both halves read before half 0 writes
@@ -519,7 +531,7 @@ void fwd_bf16_kernel(FwdParams p) {
           f32x4* o4 = reinterpret_cast<f32x4*>(dst + db * 32 + i * 8);
           *o4 = wa * *o4 + wb * ob;
         }
-      if (half == 0) *lse_dst = lse;
+      if (half_e == 0) *lse_dst = lse;
     }
   }
 }
