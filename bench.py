@@ -190,6 +190,28 @@ def time_job(job, steps, warmup):
     return wall, per_kind
 
 
+def time_cold(job, reps, flush_mib=1024):
+    """Median time of one step with the caches cold: before each step a buffer
+    larger than L2 and the last-level (MALL) cache together is overwritten, as
+    K/V chunks on a real ring arrive fresh from a neighbour.  Each step is
+    bracketed by events on the launch stream; the flush is outside them."""
+    import torch
+
+    flush = torch.empty(flush_mib * (1 << 20) // 4, device="cuda:0")
+    times = []
+    for i in range(reps):
+        flush.fill_(float(i))
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        job.run()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    del flush
+    times.sort()
+    return times[len(times) // 2]
+
+
 def summarize(job, steps, wall, per_kind):
     ms = wall * 1e3 / steps
     tflops = job.flops / (ms * 1e-3) / 1e12
@@ -433,6 +455,8 @@ def main():
     job = Job(args.workload, fused=not args.unfused)
     wall, per_kind = time_job(job, args.steps, args.warmup)
     main_res = summarize(job, args.steps, wall, per_kind)
+    # the same step with L2 and MALL flushed before it (median of 11)
+    main_res["cold_ms_per_step_median"] = time_cold(job, 11)
     log(f"bench: {args.workload}: {main_res['ms_per_step']:.3f} ms/step, {main_res['tflops']:.1f} TFLOP/s "
         f"({main_res['pct_bf16_peak']:.1f}% of bf16 peak)")
 
