@@ -39,11 +39,11 @@
 //    element j%4 of the 4-element row read by lane 4i + j/4, for i = 0..3),
 //    with addresses chosen so the key order matches the accumulator's.
 //
-// The reference max of each row is updated lazily: the exponentials of a block
-// are taken against the current reference unless some score exceeds it by
-// more than 2^8 (p <= 256 keeps fp32 exact in range and bf16 at its usual
-// relative precision); only then - or on a row's first block - is the
-// accumulator rescaled and the reference moved to the row max.  O and LSE are
+// The reference max of each row is updated lazily: it starts at the row max of
+// the first block, and the exponentials of a block are taken against the
+// current reference unless some score exceeds it by more than 2^8 (p <= 256
+// keeps fp32 exact in range and bf16 at its usual relative precision); only
+// then is the accumulator rescaled and the reference moved to the row max.  O and LSE are
 // normalised with the same reference, so the result does not depend on which
 // reference was used.
 #include "kernels.h"
@@ -266,9 +266,9 @@ void fwd_bf16_kernel(FwdParams p) {
   acc[0] = f32x16{};
   acc[1] = f32x16{};
   float m_run = -INFINITY;  // reference max of this lane's query (log2 units, scaled)
-  // Exponent offset.  Without a reference yet it is +3e38: every visible
-  // score then overflows to +inf, which sends the block down the exact path,
-  // while a fully masked row still contributes exact zeros.
+  // Exponent offset.  A row that sees no key keeps no reference: its offset
+  // stays +3e38, which still gives exact zeros for its -inf scores (and would
+  // overflow any visible score to +inf, sending it down the exact path).
   float neg_m = 3.0e38f;
   float l_run = 0.f;        // lane-partial sum of 2^(s*c - m_run)
   const float c2 = p.scale_log2;
@@ -339,11 +339,10 @@ void fwd_bf16_kernel(FwdParams p) {
   //
   // Exponentials are taken against the row's current reference max and kept
   // when every lane-partial row sum is <= 2^8 (then no score exceeded the
-  // reference by more than 8 in log2 units, so p <= 256).  Otherwise - the
-  // row's first visible block (no reference yet), or a score that outgrew the
-  // reference - the block's scores are recomputed (they are not kept live:
-  // registers), the reference is raised to the row max with acc and l
-  // rescaled, and the exponentials redone.
+  // reference by more than 8 in log2 units, so p <= 256).  Otherwise - a
+  // score outgrew the reference - the block's scores are recomputed (they are
+  // not kept live: registers), the reference is raised to the row max with acc
+  // and l rescaled, and the exponentials redone.
   //
   // Buffers: block i's keys are read at step i-1 and its values at the end of
   // step i, after the matrix work is issued, so their latency is covered by
@@ -467,6 +466,10 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<0>{}), qr[ks], S[0], 0, 0, 0);
+    // the first block's row max is the first reference, so that block takes
+    // the kept path like the others (rows that see none of it keep -inf)
+    if (0 >= nfull) mask(S[0], 0);
+    settle_reference(S[0]);
   }
   // O += V^T P^T of the last block (its values were read at the end of its step)
   auto last_pv = [&](auto j_tag, int i) __attribute__((always_inline)) {
