@@ -61,3 +61,40 @@ def test_more_than_one_gpu_is_refused():
                           capture_output=True, text=True, timeout=120)
     assert proc.returncode == 2
     assert "--gpus 2 is not supported" in proc.stderr
+
+
+def test_counter_summary_clock_and_busy(tmp_path, capsys):
+    """--counters-from: the clock comes from one XCD's busy clocks over the traced
+    duration, MFMA busy from per-SIMD busy cycles over that clock count."""
+    bench = _load_bench()
+    folder = tmp_path / "ctr"
+    dur_ns = 1_000_000                        # 1 ms per dispatch
+    clocks = 1.8e6                            # 1.8 GHz on each XCD
+    busy_frac = 0.5
+    simds = bench.N_CU * bench.SIMD_PER_CU
+    vals = {"GRBM_GUI_ACTIVE": clocks * bench.N_XCD, "SQ_VALU_MFMA_BUSY_CYCLES": busy_frac * clocks * simds,
+            "SQ_INSTS_MFMA": 1000.0, "SQ_INSTS_VALU": 8500.0, "SQ_INSTS_LDS": 1500.0,
+            "SQ_LDS_BANK_CONFLICT": 0.0, "SQ_LDS_IDX_ACTIVE": 0.25 * clocks * bench.N_CU,
+            "SQ_WAVES": 16384.0, "SQ_BUSY_CYCLES": 1.0}
+    rows = []
+    for disp in (3, 4):
+        for name, v in vals.items():
+            # each counter split over two hardware instances
+            rows.append([disp, "attnring::fwd_bf16_kernel<8>", name, v / 2])
+            rows.append([disp, "attnring::fwd_bf16_kernel<8>", name, v / 2])
+        rows.append([disp + 10, "other_kernel", "GRBM_GUI_ACTIVE", 1e12])
+    _counter_csv(folder, rows)
+    with open(folder / "ctr_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerow([3, "attnring::fwd_bf16_kernel<8>", 5_000, 5_000 + dur_ns])
+        w.writerow([4, "attnring::fwd_bf16_kernel<8>", 9_000_000, 9_000_000 + dur_ns])
+        w.writerow([13, "other_kernel", 0, 10])
+    bench.summarize_counters(str(folder))
+    rec = json.loads(capsys.readouterr().out)
+    assert rec["dispatches"] == 2
+    assert abs(rec["avg_duration_us"] - 1000.0) < 1e-9
+    assert abs(rec["shader_clock_ghz"] - 1.8) < 1e-9
+    assert abs(rec["mfma_busy_pct"] - 50.0) < 1e-9
+    assert abs(rec["valu_per_mfma"] - 8.5) < 1e-12 and abs(rec["lds_per_mfma"] - 1.5) < 1e-12
+    assert abs(rec["lds_active_pct"] - 25.0) < 1e-9 and rec["lds_bank_conflict_pct"] == 0.0
