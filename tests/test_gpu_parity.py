@@ -84,6 +84,8 @@ RING_CASES = [
     ((768,), 3, 4, 4, "normal"),         # MHA, chunks of 256
     ((1024, 512, 256, 128), 4, 8, 1, "normal"),  # varlen 8:1 (the head all-to-all share)
     ((640, 64, 192), 2, 16, 2, "normal"),        # varlen with a short sequence
+    ((768,), 4, 12, 2, "uniform"),       # GQA 6:1: two heads per workgroup
+    ((512,), 2, 12, 4, "normal"),        # GQA 3:1: one head per workgroup, kv head = head / 3
 ]
 
 
