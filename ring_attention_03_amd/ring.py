@@ -210,12 +210,20 @@ class ZigzagRing:
 
     At step t the device holds device j = (rank - t) mod N's key/value pair
     (X = chunk j, Y = chunk 2N-1-j) and its own query pair (A = chunk rank,
-    B = chunk 2N-1-rank).  A sees X only when j <= rank and never Y; B always
-    sees all of X and sees Y when j >= rank.  Each step is two launches over
-    the 2B packed query segments, each segment once per launch: {A-X, B-Y}
-    and {B-X} (A given no keys).  The first launch (the diagonal pair, j =
-    rank) writes the running state; every other launch merges into it, and a
-    launch whose keys are all in the future enqueues nothing.
+    B = chunk 2N-1-rank).  A sees X in full when j < rank, causally when
+    j = rank, and never sees Y; B sees all of X always, and Y (causally, on
+    the diagonal when j = rank) when j >= rank.  Each step is one launch over
+    the 2B packed query segments, each with one key range:
+
+    * A: the rows of X, or none when j > rank;
+    * B: X and Y together when j >= rank - they are adjacent rows of the held
+      pair - with positions counted back from Y's first key, so X's keys sit
+      just before Y's.  Every one of them is then earlier than every query
+      of B, which is exactly B's full view of X, and Y keeps its true
+      positions for the causal mask.  When j < rank, B takes X alone.
+
+    The first launch (j = rank) writes the running state; every later one
+    merges into it.
     """
 
     def __init__(self, layout: ZigzagLayout, rank: int, scale: float = 0.0):
@@ -223,36 +231,40 @@ class ZigzagRing:
             raise ValueError("rank outside the ring")
         self.layout, self.rank, self.scale = layout, rank, scale
 
-    def prepare(self, q_local, kv_pairs, o, lse, stream=None) -> "PreparedRing":
+    def step_keys(self, j: int):
+        """Per query segment (A, B per sequence): the key range and its first position at the
+        step that holds device j's pair, as (k_row0, k_len, k_pos0) lists."""
+        lay, r = self.layout, self.rank
+        cu = lay.cu()
+        kpos = lay.positions(j)
+        k_row0, k_len, k_pos0 = [], [], []
+        for b, c in enumerate(lay.chunk_lens):
+            x0, px, py = cu[2 * b], kpos[2 * b], kpos[2 * b + 1]
+            k_row0 += [x0, x0]
+            if j >= r:
+                k_len += [c if j == r else 0, 2 * c]
+                k_pos0 += [px, py - c]
+            else:
+                k_len += [c, c]
+                k_pos0 += [px, px]
+        return k_row0, k_len, k_pos0
+
+    def prepare(self, q_local, kv_pairs, o, lse, stream=None) -> "PreparedCalls":
         lay, r = self.layout, self.rank
         cu = lay.cu()
         q_pos0 = lay.positions(r)
-        nb = len(lay.seqlens)
         calls = []
         for t in range(lay.n):
             j = (r - t) % lay.n
             k_j, v_j = kv_pairs[j]
-            kpos = lay.positions(j)
-            x_row0 = [cu[2 * b] for b in range(nb)]
-            y_row0 = [cu[2 * b + 1] for b in range(nb)]
-            c = lay.chunk_lens
-            launches = [
-                # {A-X, B-Y}
-                dict(k_row0=[v for b in range(nb) for v in (x_row0[b], y_row0[b])],
-                     k_len=[v for b in range(nb) for v in (c[b], c[b])],
-                     k_pos0=[v for b in range(nb) for v in (kpos[2 * b], kpos[2 * b + 1])]),
-                # {B-X}; A gets no keys
-                dict(k_row0=[v for b in range(nb) for v in (x_row0[b], x_row0[b])],
-                     k_len=[v for b in range(nb) for v in (0, c[b])],
-                     k_pos0=[v for b in range(nb) for v in (kpos[2 * b], kpos[2 * b])]),
-            ]
-            for li, kw in enumerate(launches):
-                args = dict(cu_q=cu, q_pos0=q_pos0, scale=self.scale, causal=True, stream=stream, **kw)
-                if t == 0 and li == 0:
-                    calls.append(_native.prepare_ring_step(q_local, k_j, v_j, o, lse,
-                                                           report_skip=False, **args))
-                else:
-                    calls.append(_native.prepare_ring_step_merge(q_local, k_j, v_j, o, lse, **args))
+            k_row0, k_len, k_pos0 = self.step_keys(j)
+            args = dict(cu_q=cu, q_pos0=q_pos0, k_row0=k_row0, k_len=k_len, k_pos0=k_pos0,
+                        scale=self.scale, causal=True, stream=stream)
+            if t == 0:
+                calls.append(_native.prepare_ring_step(q_local, k_j, v_j, o, lse, report_skip=False,
+                                                       **args))
+            else:
+                calls.append(_native.prepare_ring_step_merge(q_local, k_j, v_j, o, lse, **args))
         return PreparedCalls(calls, stream)
 
     def run(self, q_local, kv_pairs, o, lse, stream=None, events=None) -> int:

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from oracle import chunk_layout_ref, visible_pairs_ref
-from ring_attention_03_amd.ring import RingAttention, RingLayout, ZigzagLayout, ring_chunk
+from ring_attention_03_amd.ring import RingAttention, RingLayout, ZigzagLayout, ZigzagRing, ring_chunk
 from ring_attention_03_amd.workloads import WORKLOADS, make_qkv, sample_rows
 
 
@@ -155,3 +155,31 @@ def test_zigzag_layout_matches_oracle_chunks_and_balances_work(seqlens, n):
         assert zz.visible_pairs(r) == (visible_pairs_ref(seqlens, 2 * n, r)
                                        + visible_pairs_ref(seqlens, 2 * n, 2 * n - 1 - r))
     assert len({zz.visible_pairs(r) for r in range(n)}) == 1
+
+
+@pytest.mark.parametrize("seqlens,n", [((64,), 4), ((40, 24), 2), ((48,), 3)])
+def test_zigzag_step_keys_give_exactly_the_causal_pairs(seqlens, n):
+    # for every step, query row and key row of the held pair: the key range and
+    # positions a launch is given, with the causal mask applied to them, select
+    # exactly the keys whose true positions are visible to the query
+    zz = ZigzagLayout(seqlens, n)
+    cu = zz.cu()
+    for r in range(n):
+        ring = ZigzagRing(zz, r)
+        q_pos = zz.positions(r)
+        for t in range(n):
+            j = (r - t) % n
+            k_row0, k_len, k_pos0 = ring.step_keys(j)
+            true_kpos = zz.positions(j)
+            for b, c in enumerate(zz.chunk_lens):
+                pair_rows = range(cu[2 * b], cu[2 * b + 2])
+                true_pos = {row: true_kpos[2 * b + (row - cu[2 * b]) // c] + (row - cu[2 * b]) % c
+                            for row in pair_rows}
+                for seg in (2 * b, 2 * b + 1):
+                    given = range(k_row0[seg], k_row0[seg] + k_len[seg])
+                    assert set(given) <= set(pair_rows)
+                    for i in range(c):
+                        pq = q_pos[seg] + i
+                        picked = {row for row in given if k_pos0[seg] + (row - k_row0[seg]) <= pq}
+                        truth = {row for row in pair_rows if true_pos[row] <= pq}
+                        assert picked == truth, (r, t, b, seg, i)
