@@ -349,6 +349,20 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload
 N_CU, N_XCD, SIMD_PER_CU = 256, 8, 4
 
 
+def _counters_present(folder, name_part):
+    """Names of the counters recorded for kernels matching ``name_part`` in a --pmc run."""
+    import csv
+    import glob
+
+    names = set()
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if name_part in r["Kernel_Name"]:
+                    names.add(r["Counter_Name"])
+    return names
+
+
 def summarize_counters(folder):
     """Derived figures of the attention kernel from one rocprofv3 --pmc --kernel-trace run.
 
@@ -357,14 +371,21 @@ def summarize_counters(folder):
     of every XCD, so one XCD's share over the traced duration gives the
     shader clock; SQ_VALU_MFMA_BUSY_CYCLES counts per SIMD, so dividing by
     that clock count times the SIMD count gives the matrix cores' busy
-    fraction at the clock the kernel actually ran.
+    fraction at the clock the kernel actually ran.  The figures of whichever
+    further counters the run holds are added: LDS (SQ_INSTS_LDS,
+    SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE) or vector ALU
+    (SQ_ACTIVE_INST_VALU in quad-cycles per wave, SQ_VALU_MFMA_COEXEC_CYCLES:
+    cycles with the matrix core busy and a vector instruction issued).
     """
     import csv
     import glob
 
-    names = ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
-             "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAVES", "SQ_BUSY_CYCLES"]
-    vals = {n: _counter_per_dispatch(folder, n, DOMINANT_KERNEL)[0] for n in names}
+    present = _counters_present(folder, DOMINANT_KERNEL)
+    need = ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA"]
+    missing = [n for n in need if n not in present]
+    if missing:
+        raise SystemExit(f"counters {missing} missing for {DOMINANT_KERNEL} under {folder}")
+    vals = {n: _counter_per_dispatch(folder, n, DOMINANT_KERNEL)[0] for n in sorted(present)}
     durs = []
     for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
         with open(path, newline="") as f:
@@ -376,17 +397,28 @@ def summarize_counters(folder):
     dur = sum(durs) / len(durs)
     clocks = vals["GRBM_GUI_ACTIVE"] / N_XCD
     simds = N_CU * SIMD_PER_CU
-    mfma_busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (clocks * simds)
+    mfma = vals["SQ_INSTS_MFMA"]
     rec = {"kernel": DOMINANT_KERNEL, "kernel_source_sha": kernel_source_hash(), "dispatches": len(durs),
            "avg_duration_us": dur * 1e6, "shader_clock_ghz": clocks / dur / 1e9,
-           "mfma_busy_pct": 100.0 * mfma_busy,
-           "mfma_instructions": vals["SQ_INSTS_MFMA"],
-           "valu_per_mfma": vals["SQ_INSTS_VALU"] / vals["SQ_INSTS_MFMA"],
-           "lds_per_mfma": vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"],
-           "lds_bank_conflict_pct": 100.0 * vals["SQ_LDS_BANK_CONFLICT"] / max(vals["SQ_LDS_IDX_ACTIVE"], 1.0),
-           "lds_active_pct": 100.0 * vals["SQ_LDS_IDX_ACTIVE"] / (clocks * N_CU),
-           "waves": vals["SQ_WAVES"],
-           "raw": vals}
+           "mfma_busy_pct": 100.0 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (clocks * simds),
+           "mfma_instructions": mfma}
+    if "SQ_INSTS_VALU" in vals:
+        rec["valu_per_mfma"] = vals["SQ_INSTS_VALU"] / mfma
+    if "SQ_INSTS_VALU_TRANS_F32" in vals:
+        rec["trans_per_mfma"] = vals["SQ_INSTS_VALU_TRANS_F32"] / mfma
+    if "SQ_INSTS_LDS" in vals:
+        rec["lds_per_mfma"] = vals["SQ_INSTS_LDS"] / mfma
+    if "SQ_LDS_IDX_ACTIVE" in vals:
+        rec["lds_active_pct"] = 100.0 * vals["SQ_LDS_IDX_ACTIVE"] / (clocks * N_CU)
+        if "SQ_LDS_BANK_CONFLICT" in vals:
+            rec["lds_bank_conflict_pct"] = 100.0 * vals["SQ_LDS_BANK_CONFLICT"] / max(vals["SQ_LDS_IDX_ACTIVE"], 1.0)
+    if "SQ_ACTIVE_INST_VALU" in vals:
+        rec["valu_active_pct"] = 100.0 * 4 * vals["SQ_ACTIVE_INST_VALU"] / (clocks * simds)
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in vals:
+        rec["mfma_coexec_pct_of_busy"] = 100.0 * vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / vals["SQ_VALU_MFMA_BUSY_CYCLES"]
+    if "SQ_WAVES" in vals:
+        rec["waves"] = vals["SQ_WAVES"]
+    rec["raw"] = vals
     print(json.dumps(rec, indent=1), flush=True)
 
 
