@@ -151,7 +151,8 @@ class Job:
 
     def config(self):
         w = self.w
-        return {"workload": self.name, "mode": w.mode, "seq_lens": list(w.seqlens), "ring_chunks": w.n_chunks,
+        return {"workload": self.name, "description": w.note, "mode": w.mode, "seq_lens": list(w.seqlens),
+                "ring_chunks": w.n_chunks,
                 "rank": self.rank, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                 "head_dim": w.head_dim, "causal": True, "local_q_rows": int(self.q.shape[0]),
                 "algorithmic_tflop": self.flops / 1e12,

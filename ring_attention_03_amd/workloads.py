@@ -45,6 +45,10 @@ class Workload:
     mode: str = "ring"
     note: str = field(default="", compare=False)
 
+    def __post_init__(self):
+        if self.mode not in ("ring", "chunked", "zigzag"):
+            raise ValueError(f"workload {self.name}: unknown mode {self.mode!r}")
+
     @property
     def total_tokens(self) -> int:
         return int(sum(self.seqlens))
@@ -56,19 +60,19 @@ class Workload:
 
 WORKLOADS = {
     "tiny_ring_512": Workload(
-        "tiny_ring_512", (512,), 4, None, 4, 1, 64, "fp32", "normal", 1,
+        "tiny_ring_512", (512,), 4, None, 4, 1, 64, "fp32", "normal", 1, "ring",
         "S=512 in 4 ring chunks of 128, GQA 4:1, fp32; every rank"),
     "ring_32k_rank3": Workload(
-        "ring_32k_rank3", (32768,), 8, 3, 64, 8, 64, "bf16", "normal", 2,
+        "ring_32k_rank3", (32768,), 8, 3, 64, 8, 64, "bf16", "normal", 2, "ring",
         "S=32768 in 8 chunks of 4096, rank 3 against all 8 chunks"),
     "ring_64k_rank7": Workload(
-        "ring_64k_rank7", (65536,), 8, 7, 64, 8, 64, "bf16", "uniform", 3,
+        "ring_64k_rank7", (65536,), 8, 7, 64, 8, 64, "bf16", "uniform", 3, "ring",
         "S=65536 in 8 chunks of 8192, last rank (heaviest causal share)"),
     "prefill_100k": Workload(
-        "prefill_100k", (102400,), 1, 0, 64, 8, 64, "bf16", "normal", 4,
+        "prefill_100k", (102400,), 1, 0, 64, 8, 64, "bf16", "normal", 4, "ring",
         "S=102400 full causal prefill in one call"),
     "ring_100k_n16": Workload(
-        "ring_100k_n16", (102400,), 16, None, 64, 8, 64, "bf16", "normal", 4,
+        "ring_100k_n16", (102400,), 16, None, 64, 8, 64, "bf16", "normal", 4, "ring",
         "S=102400 in 16 ring chunks of 6400, every rank"),
     "ring_64k_zigzag_rank7": Workload(
         "ring_64k_zigzag_rank7", (65536,), 8, 7, 64, 8, 64, "bf16", "uniform", 3, "zigzag",
