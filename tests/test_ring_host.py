@@ -183,3 +183,11 @@ def test_zigzag_step_keys_give_exactly_the_causal_pairs(seqlens, n):
                         picked = {row for row in given if k_pos0[seg] + (row - k_row0[seg]) <= pq}
                         truth = {row for row in pair_rows if true_pos[row] <= pq}
                         assert picked == truth, (r, t, b, seg, i)
+
+
+def test_workload_modes_are_explicit_and_validated():
+    from ring_attention_03_amd.workloads import WORKLOADS
+    assert {w.mode for w in WORKLOADS.values()} == {"ring", "chunked", "zigzag"}
+    assert all(w.note for w in WORKLOADS.values())
+    with pytest.raises(ValueError):
+        WORKLOADS["ring_64k_rank7"].scaled(mode="contiguous")
