@@ -58,6 +58,9 @@ def parse_args():
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only measure the sustained rate of a large library bf16 GEMM on random data "
                          "(the practical matrix-core ceiling under the board's power limit)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the sustained rate of back-to-back bf16 MFMAs on constant and on "
+                         "random operands (the probe library built beside the attention library)")
     ap.add_argument("--counters-from", metavar="FOLDER",
                     help="only summarize a rocprofv3 --pmc --kernel-trace run of this script "
                          "(MFMA busy, LDS bank conflicts, shader clock) for the attention kernel")
@@ -456,6 +459,50 @@ def gemm_ceiling():
                       "ms": ms, "tflops": tf, "pct_bf16_peak": 100.0 * tf / PEAK_BF16_TFLOPS}), flush=True)
 
 
+def mfma_ceiling():
+    """Sustained rate of back-to-back 32x32x16 bf16 MFMAs on constant and on random operands.
+
+    Two workgroups of 4 waves per CU (two waves per SIMD, all resident at
+    once, so there is no tail of late workgroups), each wave doing 16 MFMAs
+    per iteration on four independent accumulators; each case first runs for
+    3 s so the clock settles under its own load.
+    """
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "ring_attention_03_amd", "libattnprobe.so"))
+    lib.attn_probe_mfma.restype = ctypes.c_int
+    lib.attn_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 4096
+    out = torch.empty(blocks * 256, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for name, random in (("constant_operands", 0), ("random_operands", 1)):
+        def launch():
+            st = lib.attn_probe_mfma(ctypes.c_void_p(out.data_ptr()), blocks, random, iters, stream)
+            if st != 0:
+                raise RuntimeError(f"attn_probe_mfma failed with HIP error {st}")
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 3.0:
+            launch()
+            torch.cuda.synchronize()
+        reps = 20
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            launch()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        flops = blocks * 4 * iters * 16 * 2.0 * 32 * 32 * 16
+        res[name] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
+    res["pct_bf16_peak"] = {k: 100.0 * v["tflops"] / PEAK_BF16_TFLOPS for k, v in res.items()}
+    print(json.dumps({"mfma": "v_mfma_f32_32x32x16_bf16, 2 waves per SIMD, 16 per iteration, 4 accumulators",
+                      **res}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.counters_from:
@@ -478,6 +525,9 @@ def main():
         return
     if args.gemm_ceiling:
         gemm_ceiling()
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
     from ring_attention_03_amd import load_library
 

@@ -1,7 +1,8 @@
-"""Build ``libattnring.so`` in-tree with hipcc for gfx950.
+"""Build ``libattnring.so`` (and the measurement probe ``libattnprobe.so``)
+in-tree with hipcc for gfx950.
 
 Usage: ``python -m ring_attention_03_amd.build`` (or ``__graft_entry__.build()``).
-Each source compiles to an object in parallel, then one shared library is
+Each source compiles to an object in parallel, then each shared library is
 linked next to this file.  All device code is built without packed-fp32
 instructions.
 """
@@ -19,6 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattnring.so")
 SOURCES = ["fwd_bf16.hip", "fwd_f32.hip", "merge.hip", "abi.cpp"]
+# matrix-core rate probe used by bench.py --mfma-ceiling; not part of the attention ABI
+PROBE_LIB = os.path.join(PKG, "libattnprobe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -43,10 +47,10 @@ def _compile_cmd(src: str) -> tuple[list[str], str]:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    procs, objs = [], []
-    for src in SOURCES:
+    procs, objs = [], {}
+    for src in SOURCES + PROBE_SOURCES:
         cmd, obj = _compile_cmd(src)
-        objs.append(obj)
+        objs[src] = obj
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -63,12 +67,13 @@ def build(verbose: bool = False) -> str:
             print("\n".join(lines))
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
-    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(link), flush=True)
-    subprocess.run(link, check=True)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[objs[x] for x in srcs], "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

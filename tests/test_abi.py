@@ -200,3 +200,14 @@ def test_prefill_and_merge_validation():
     assert lib.attn_ring_merge(-1, 4, 64, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None) == 1
     assert lib.attn_ring_merge(0, 4, 64, None, None, None, None, None) == 0  # nothing to do
     del keep
+
+
+def test_probe_library_is_built_apart_from_the_abi():
+    # the matrix-core probe used by bench.py lives in its own library, so the
+    # attention library exports exactly the declared ABI
+    import os
+
+    probe = os.path.join(os.path.dirname(_native.__file__), "libattnprobe.so")
+    lib = ctypes.CDLL(probe)
+    assert hasattr(lib, "attn_probe_mfma")
+    assert not hasattr(_native.load_library(), "attn_probe_mfma")
