@@ -276,6 +276,26 @@ def test_very_negative_scores_keep_their_softmax():
     assert_close(o, lse, o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, "very negative scores")
 
 
+def test_growing_scores_rescale_every_block():
+    # Scores grow along the keys (key i scores about 150*i/t against every
+    # query), so each 32-key block exceeds the running reference by far more
+    # than 2^8 and every block takes the rescale path; the softmax of each row
+    # is dominated by its own latest keys.
+    g = torch.Generator().manual_seed(22)
+    t = 512
+    u = torch.randn(64, generator=g)
+    u = u / u.norm()
+    ramp = torch.arange(t, dtype=torch.float32)[:, None, None] / t
+    k = 40.0 * ramp * u + 0.05 * torch.randn(t, 2, 64, generator=g)
+    q = 30.0 * u + 0.5 * torch.randn(t, 8, 64, generator=g)
+    v = torch.randn(t, 2, 64, generator=g)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    o, lse = _prefill(q, k, v)
+    o_ref, lse_ref = causal_attention_ref(q, k, v)
+    assert float(lse_ref[:, -1].min()) > 100  # the last rows' scores really are that large
+    assert_close(o, lse, o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, "scores growing along the keys")
+
+
 def test_fully_masked_step_skips_or_writes_identity():
     g = torch.Generator().manual_seed(16)
     q = torch.randn(100, 8, 64, generator=g).to(torch.bfloat16).cuda()
