@@ -218,6 +218,17 @@ def test_prefill_matches_oracle(seqlens, hq, hkv, dtype):
     assert_close(o, lse, o_ref, lse_ref, *tol, f"prefill {seqlens}")
 
 
+def test_prefill_with_the_most_sequences_a_call_takes():
+    # 64 packed sequences (the per-call maximum) of ragged lengths 1..97
+    seqlens = tuple(1 + (37 * i) % 97 for i in range(64))
+    w = WORKLOADS["prefill_100k"].scaled(seqlens=seqlens, num_q_heads=8, num_kv_heads=1, seed=23)
+    q, k, v = make_qkv(w)
+    log(f"prefill of {len(seqlens)} sequences, {sum(seqlens)} rows")
+    o, lse = _prefill(q, k, v, seqlens)
+    o_ref, lse_ref = causal_attention_ref(q, k, v, seqlens)
+    assert_close(o, lse, o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, "64 sequences")
+
+
 def test_prefill_equals_ring_of_16():
     w = WORKLOADS["ring_100k_n16"].scaled(seqlens=(1024,), seed=13)
     q, k, v = make_qkv(w)
