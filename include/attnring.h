@@ -12,6 +12,8 @@
  *
  *   attn_ring_step      - attention of the local query block against ONE
  *                         key/value block, producing a partial (O, LSE);
+ *   attn_ring_step_merge - the same step folded straight into a running
+ *                         (O, LSE) in place, with no partial buffers;
  *   attn_ring_merge     - folds a partial (O, LSE) into a running one;
  *   attn_prefill_causal - full causal attention in one call (the result the
  *                         ring must reproduce, and the N = 1 case).
