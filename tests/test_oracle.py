@@ -307,7 +307,9 @@ def test_chunk_layout_and_pair_count():
         brute_total = sum(p + 1 for s in seqlens for p in range(s))
         assert visible_pairs_ref(seqlens) == brute_total
         assert sum(visible_pairs_ref(seqlens, n, r) for r in range(n)) == brute_total
-    # the survey's pair counts of the long workloads
+    # closed forms for the long workloads: rank r of N chunks of c sees r*c*c + c*(c+1)/2
+    # pairs (65536/8 rank 7: 7*8192^2 + 8192*8193/2); a whole prompt S sees S*(S+1)/2
     assert visible_pairs_ref([65536], 8, 7) == 503_320_576
     assert visible_pairs_ref([32768], 8, 3) == 58_722_304
     assert visible_pairs_ref([102400]) == 5_242_931_200
+    assert 7 * 8192 ** 2 + 8192 * 8193 // 2 == 503_320_576 and 102400 * 102401 // 2 == 5_242_931_200
