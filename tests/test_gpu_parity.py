@@ -76,6 +76,19 @@ def test_tiny_ring_fp32_every_rank():
         assert_close(o, lse, full_o[rows], full_lse[:, rows], TOL_F32, TOL_F32, "vs unchunked")
 
 
+def test_fp32_ring_ragged_tiles_every_rank():
+    # the fp32 kernel over many row tiles with ragged tails: chunks of 125 rows,
+    # GQA 8:1, a varlen pair of sequences
+    w = WORKLOADS["tiny_ring_512"].scaled(seqlens=(1000, 500), n_chunks=4, num_q_heads=16,
+                                          num_kv_heads=2, seed=24)
+    q, k, v = make_qkv(w)
+    for r in range(w.n_chunks):
+        log(f"fp32 ring {w.seqlens} N=4 16/2 rank {r}")
+        o, lse = run_ring(q, k, v, w.seqlens, w.n_chunks, r, fused=(r % 2 == 0))
+        o_ref, lse_ref = ring_ref(q, k, v, w.seqlens, w.n_chunks, r)
+        assert_close(o, lse, o_ref, lse_ref, TOL_F32, TOL_F32, f"fp32 ring rank {r}")
+
+
 # ---------------------------------------------------------------------------- bf16 rings, reduced size
 RING_CASES = [
     # (seqlens, N, Hq, Hkv, v_dist) -- shapes of the long workloads, scaled down
