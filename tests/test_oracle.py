@@ -216,6 +216,22 @@ def test_merge_identity_commutative_associative():
     assert (both_empty[0] == 0).all() and np.isneginf(both_empty[1]).all()
 
 
+def test_merge_closed_forms():
+    # Two copies of the same partial are the same keys twice: the weights stay
+    # the same (O unchanged) and the normaliser doubles (LSE + ln 2).  Partials
+    # whose LSEs differ by ln 3 weigh 3:1.  Huge LSEs must not overflow.
+    o, lse = rand((5, 2, 4), 60), rand((2, 5), 61)
+    m_o, m_l = merge_ref(o, lse, o, lse)
+    np.testing.assert_allclose(m_o, o, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(m_l, lse + math.log(2.0), rtol=0, atol=1e-14)
+    o2 = rand((5, 2, 4), 62)
+    big = np.full((2, 5), 800.0)
+    m_o, m_l = merge_ref(o, big + math.log(3.0), o2, big)
+    # (LSEs of 800 carry ~800 * 2^-53 = 1e-13 of rounding into the weights' exponents)
+    np.testing.assert_allclose(m_o, 0.75 * o + 0.25 * o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m_l, big + math.log(4.0), rtol=0, atol=1e-12)
+
+
 def test_merge_of_disjoint_key_sets_is_full_softmax():
     # Split the keys of a non-causal problem into two sets: the merge must equal the whole.
     q, k, v = rand((6, 2, 5), 50), rand((10, 1, 5), 51), rand((10, 1, 5), 52)
