@@ -39,13 +39,17 @@
 //    element j%4 of the 4-element row read by lane 4i + j/4, for i = 0..3),
 //    with addresses chosen so the key order matches the accumulator's.
 //
-// The reference max of each row is updated lazily: it starts at the row max of
-// the first block, and the exponentials of a block are taken against the
-// current reference unless some score exceeds it by more than 2^8 (p <= 256
-// keeps fp32 exact in range and bf16 at its usual relative precision); only
-// then is the accumulator rescaled and the reference moved to the row max.  O and LSE are
-// normalised with the same reference, so the result does not depend on which
-// reference was used.
+// The reference max of each row is updated lazily.  It starts at the row max
+// of the first 128-key tile, so that tile's weights are all <= 1 and the
+// largest is exactly 1.  A later block's exponentials are taken against the
+// current reference and kept unless, in some lane, their sum exceeds the
+// lane's accumulated sum (at least 1, at most 2^8); only then is the
+// accumulator rescaled and the reference moved to the row max.  So no kept
+// block carries more weight than the keys before it: a key that would dominate
+// the row moves the reference onto itself and enters with weight exactly 1,
+// not with a weight rounded to bf16 (relative error up to 2^-8), which would
+// shift O by up to 2^-8 |v|.  O and LSE are normalised with the same
+// reference, so the result does not depend on which reference was used.
 #include "kernels.h"
 #include "merge_math.h"
 
@@ -63,8 +67,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
 
 constexpr int D = kHeadDim;       // 64
-constexpr int NW = 8;             // waves per workgroup
-constexpr int QW = 32;            // query rows per wave
+constexpr int NW = kBf16Waves;    // waves per workgroup (8)
+constexpr int QW = kBf16RowsPerWave;  // query rows per wave (32)
 constexpr int BT = 128;           // keys per LDS tile
 constexpr int BPT = BT / 32;      // 32-key blocks per tile
 
@@ -72,7 +76,7 @@ constexpr int NKB = 2;            // key tile buffers in LDS
 constexpr int NVB = 3;            // value tile buffers in LDS (values are read one tile later)
 constexpr int TILE_ELEMS = BT * D;
 constexpr int TILE_BYTES = TILE_ELEMS * 2;
-constexpr float SUM_LIMIT = 256.0f;  // a block's exponentials are kept when each lane-partial sum is <= 2^8
+constexpr float SUM_LIMIT = 256.0f;  // no block's exponentials are kept when a lane-partial sum exceeds 2^8
 
 // LDS tile layout: row-major [key][64], 16-byte chunks XOR-swizzled per row so
 // that the MFMA operand reads hit distinct banks.  The LDS serves 256 bytes
@@ -315,12 +319,16 @@ void fwd_bf16_kernel(FwdParams p) {
       Sb[e] = off <= lim ? Sb[e] : -INFINITY;
     }
   };
-  // raise the reference max of each row to the row max of Sb (rescaling acc and l)
-  auto settle_reference = [&](const f32x16& Sb) __attribute__((always_inline)) {
-    float mx = fmaxf(fmaxf(Sb[0], Sb[1]), Sb[2]);  // chains of 3-input max over the lane's 16 keys
+  // max of the lane's 16 scores (chains of 3-input max)
+  auto lane_max = [&](const f32x16& Sb) __attribute__((always_inline)) {
+    float mx = fmaxf(fmaxf(Sb[0], Sb[1]), Sb[2]);
 #pragma unroll
     for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, Sb[e]), Sb[e + 1]);
-    mx = fmaxf(mx, Sb[15]);
+    return fmaxf(mx, Sb[15]);
+  };
+  // raise the reference max of each row to the row max whose lane maxima are mx
+  // (rescaling acc and l)
+  auto raise_reference = [&](float mx) __attribute__((always_inline)) {
     const float m_new = fmaxf(m_run, max_halves(mx) * c2);
     if (m_new > m_run) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was -inf
@@ -331,6 +339,7 @@ void fwd_bf16_kernel(FwdParams p) {
       neg_m = -m_new;
     }
   };
+  auto settle_reference = [&](const f32x16& Sb) __attribute__((always_inline)) { raise_reference(lane_max(Sb)); };
 
   // One step of the software pipeline for block i (i % 4 == J, compile-time).
   // The softmax of block i runs on the vector ALU while the matrix core does
@@ -338,11 +347,11 @@ void fwd_bf16_kernel(FwdParams p) {
   // half); both are independent of block i, so one wave keeps both units fed.
   //
   // Exponentials are taken against the row's current reference max and kept
-  // when every lane-partial row sum is <= 2^8 (then no score exceeded the
-  // reference by more than 8 in log2 units, so p <= 256).  Otherwise - a
-  // score outgrew the reference - the block's scores are recomputed (they are
-  // not kept live: registers), the reference is raised to the row max with acc
-  // and l rescaled, and the exponentials redone.
+  // when every lane-partial row sum is <= the lane's accumulated sum (clamped
+  // to [1, 2^8]), so p <= 256 and the block does not dominate the row.
+  // Otherwise - a score outgrew the reference - the block's scores are
+  // recomputed (they are not kept live: registers), the reference is raised to
+  // the row max with acc and l rescaled, and the exponentials redone.
   //
   // Buffers: block i's keys are read at step i-1 and its values at the end of
   // step i, after the matrix work is issued, so their latency is covered by
@@ -418,7 +427,11 @@ void fwd_bf16_kernel(FwdParams p) {
     // among this step's instructions instead of trailing it
     asm volatile("" ::"v"(P[CUR][0]), "v"(P[CUR][1]));
     float rs = (part[0] + part[1]) + (part[2] + part[3]);
-    if (__builtin_amdgcn_ballot_w64(rs > SUM_LIMIT) != 0) {  // wave-uniform, rare
+    // keep limit: the lane's accumulated sum, clamped to [1, 2^8]; the first
+    // tile's blocks are all <= the reference (it is their row max), so they only
+    // need the 2^8 guard (a row that saw none of them has no reference yet)
+    const float keep = __builtin_amdgcn_fmed3f(l_run, i < BPT ? SUM_LIMIT : 1.0f, SUM_LIMIT);
+    if (__builtin_amdgcn_ballot_w64(rs > keep) != 0) {  // wave-uniform, rare
       f32x16& Sb = S[CUR];
       Sb = f32x16{};
       if constexpr (J == 3) {
@@ -462,14 +475,24 @@ void fwd_bf16_kernel(FwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the queries and this wave's share of tile 0
     __syncthreads();
     if (ntile > 1) copy_tile(1);
-    S[0] = f32x16{};
+    // the row max over the first tile is the first reference, so its blocks
+    // take the kept path with every weight <= 1 (rows that see none of it keep
+    // -inf); block 0's scores are computed last and stay in S[0]
+    auto first_scores = [&](auto b_tag) __attribute__((always_inline)) {
+      constexpr int B = decltype(b_tag)::value;
+      S[0] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<0>{}), qr[ks], S[0], 0, 0, 0);
-    // the first block's row max is the first reference, so that block takes
-    // the kept path like the others (rows that see none of it keep -inf)
-    if (0 >= nfull) mask(S[0], 0);
-    settle_reference(S[0]);
+      for (int ks = 0; ks < 4; ++ks)
+        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<B>{}), qr[ks], S[0], 0, 0, 0);
+      if (B >= nfull) mask(S[0], B);
+      return lane_max(S[0]);
+    };
+    static_assert(BPT == 4, "the first reference spans the four blocks of a tile");
+    float mx = first_scores(Int<3>{});
+    mx = fmaxf(mx, first_scores(Int<2>{}));
+    mx = fmaxf(mx, first_scores(Int<1>{}));
+    mx = fmaxf(mx, first_scores(Int<0>{}));
+    raise_reference(mx);
   }
   // O += V^T P^T of the last block (its values were read at the end of its step)
   auto last_pv = [&](auto j_tag, int i) __attribute__((always_inline)) {
@@ -540,16 +563,6 @@ void fwd_bf16_kernel(FwdParams p) {
 }
 
 }  // namespace
-
-Bf16Geometry bf16_geometry(int hq, int hkv) {
-  const int group = hq / hkv;
-  Bf16Geometry g;
-  g.waves = NW;
-  g.rows_per_wave = QW;
-  // heads per workgroup: largest of 8, 4, 2, 1 dividing the GQA group size
-  g.heads_per_group = (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
-  return g;
-}
 
 hipError_t launch_fwd_bf16(const FwdParams& p, const Bf16Geometry& geo, int n_units,
                            hipStream_t stream) {
