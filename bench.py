@@ -39,12 +39,17 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="ring_64k_rank7")
-    ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,varlen_ulysses_rank7,chunked_prefill_12k,"
-                    "ring_64k_zigzag_rank7",
+    ap.add_argument("--extra", default="ring_32k_rank3,prefill_100k,ring_100k_n16_rank15,ring_100k_n16,"
+                    "varlen_ulysses_rank7,chunked_prefill_12k,ring_64k_zigzag_rank7",
                     help="comma list of further workloads measured in the same run ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--extra-warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache passes (for profiled runs: only warmup and timed steps launch)")
+    ap.add_argument("--trace-from", metavar="FOLDER",
+                    help="only summarize the attention kernel's durations in a rocprofv3 --kernel-trace run of "
+                         "this script with the same --workload/--warmup/--steps and --extra ''")
     ap.add_argument("--unfused", action="store_true",
                     help="merge each ring step with the separate merge kernel instead of in the step")
     ap.add_argument("--cpu-rows", type=int, default=768,
@@ -61,6 +66,9 @@ def parse_args():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only measure the sustained rate of back-to-back bf16 MFMAs on constant and on "
                          "random operands (the probe library built beside the attention library)")
+    ap.add_argument("--valu-rates", action="store_true",
+                    help="only measure issue rates of the softmax's vector instructions and their overlap "
+                         "with the matrix cores (the probe library built beside the attention library)")
     ap.add_argument("--counters-from", metavar="FOLDER",
                     help="only summarize a rocprofv3 --pmc --kernel-trace run of this script "
                          "(MFMA busy, LDS bank conflicts, shader clock) for the attention kernel")
@@ -93,6 +101,8 @@ class Job:
         dev = torch.device("cuda:0")
         self.layout = RingLayout(w.seqlens, w.n_chunks)
         self.rank = 0 if w.rank is None else w.rank
+        # a ring workload without a rank is the whole ring: every device's share, one after another
+        self.sweep = w.mode == "ring" and w.rank is None and w.n_chunks > 1
         lay = self.layout
         if w.n_chunks == 1:
             self.q = q.to(dev)
@@ -108,6 +118,11 @@ class Job:
             self.q = lay.gather(q, self.rank).to(dev).contiguous()
             self.k = lay.gather_prefix(k, self.rank).to(dev).contiguous()
             self.v = lay.gather_prefix(v, self.rank).to(dev).contiguous()
+        elif self.sweep:
+            self.chunks = [(lay.gather(k, j).to(dev).contiguous(), lay.gather(v, j).to(dev).contiguous())
+                           for j in range(w.n_chunks)]
+            self.q_ranks = [lay.gather(q, r).to(dev).contiguous() for r in range(w.n_chunks)]
+            self.q = self.q_ranks[-1]
         else:
             self.q = lay.gather(q, self.rank).to(dev).contiguous()
             self.chunks = [(lay.gather(k, j).to(dev).contiguous(), lay.gather(v, j).to(dev).contiguous())
@@ -119,7 +134,10 @@ class Job:
         self.o_p = self.lse_p = None
         if w.n_chunks > 1 and w.mode == "ring" and not fused:
             self.o_p, self.lse_p = torch.empty_like(self.o), torch.empty_like(self.lse)
-        self.pairs = (self.zigzag[0] if w.mode == "zigzag" else lay).visible_pairs(self.rank)
+        if self.sweep:
+            self.pairs = sum(lay.visible_pairs(r) for r in range(w.n_chunks))
+        else:
+            self.pairs = (self.zigzag[0] if w.mode == "zigzag" else lay).visible_pairs(self.rank)
         self.flops = 4 * w.head_dim * w.num_q_heads * self.pairs
         # every launch's arguments are marshalled once: the timed loop only enqueues
         if w.n_chunks == 1:
@@ -132,6 +150,12 @@ class Job:
                                                                   self.lse)
         elif w.mode == "zigzag":
             self.prepared = self.zigzag[1].prepare(self.q, self.chunks, self.o, self.lse)
+        elif self.sweep:
+            self.outs = [(torch.empty(x.shape[0], hq, d, device=dev), torch.empty(hq, x.shape[0], device=dev))
+                         for x in self.q_ranks]
+            self.prepared_all = [RingAttention(lay, r).prepare(self.q_ranks[r], self.chunks, *self.outs[r],
+                                                               fused=fused)
+                                 for r in range(w.n_chunks)]
         else:
             self.prepared = self.ring.prepare(self.q, self.chunks, self.o, self.lse, self.o_p,
                                               self.lse_p, fused=fused)
@@ -147,16 +171,20 @@ class Job:
                 e.record()
                 events.append(("step", s, e))
             return 1
+        if self.sweep:
+            return sum(p.run(events=events, event_pool=event_pool) for p in self.prepared_all)
         return self.prepared.run(events=events, event_pool=event_pool)
 
     def launches_per_step(self):
+        if self.sweep:
+            return 2 * self.w.n_chunks * self.w.n_chunks
         return 1 if self.w.n_chunks == 1 or self.w.mode == "chunked" else 2 * self.w.n_chunks
 
     def config(self):
         w = self.w
         return {"workload": self.name, "description": w.note, "mode": w.mode, "seq_lens": list(w.seqlens),
                 "ring_chunks": w.n_chunks,
-                "rank": self.rank, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                "rank": "all (one after another)" if self.sweep else self.rank, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                 "head_dim": w.head_dim, "causal": True, "local_q_rows": int(self.q.shape[0]),
                 "algorithmic_tflop": self.flops / 1e12,
                 "merge": "in the step kernel" if self.fused else "separate merge kernel"}
@@ -503,8 +531,145 @@ def mfma_ceiling():
                       **res}), flush=True)
 
 
+# probe modes of attn_probe_valu: (name, MFMAs per iteration, vector instructions per iteration)
+VALU_PROBES = [
+    ("v_fma_f32", 0, 32), ("v_exp_f32", 0, 32), ("v_add_f32", 0, 32), ("v_cvt_pk_bf16_f32", 0, 32),
+    ("v_dot2c_f32_bf16", 0, 32), ("v_max3_f32", 0, 32),
+    ("mfma_32x32x16_bf16", 16, 0), ("mfma_16x16x32_bf16", 16, 0),
+    ("block_mix: 8 mfma + 16 fma + 16 exp + 16 add + 8 cvt", 8, 56),
+    ("block_mix_without_exp: 8 mfma + 16 fma + 16 add + 8 cvt", 8, 40),
+    ("block_mix_without_mfma: 16 fma + 16 exp + 16 add + 8 cvt", 0, 56),
+    ("mfma_with_fma: 8 mfma + 32 fma", 8, 32),
+    ("mfma_with_exp: 8 mfma + 16 exp", 8, 16),
+    ("mfma_with_fma64: 8 mfma + 64 fma", 8, 64),
+    ("split_roles: 8 mfma in one wave, 16 fma + 16 exp + 16 add + 8 cvt in another, per SIMD", 8, 56),
+    ("block_mix_poly_exp: 8 mfma + 16 fma + 16 cubic exp2 + 16 add + 8 cvt", 8, 168),
+    ("block_mix_16x16x32: 16 mfma 16x16x32 + 16 fma + 16 exp + 16 add + 8 cvt", 8, 56),
+    ("mfma_agpr_with_fma: 8 mfma (AGPR accumulators) + 32 fma", 8, 32),
+    ("block_mix_agpr: 8 mfma (AGPR accumulators) + 16 fma + 16 exp + 16 add + 8 cvt", 8, 56),
+    ("mfma16_with_fma: 16 mfma 16x16x32 + 32 fma", 8, 32),
+    ("mfma_ab_agpr_with_fma: 8 mfma (A, B, C in AGPRs) + 32 fma", 8, 32),
+    ("block_mix_ab_agpr: 8 mfma (A, B, C in AGPRs) + 16 fma + 16 exp + 16 add + 8 cvt", 8, 56),
+    ("block_mix_a_agpr: 8 mfma (A, C in AGPRs) + 16 fma + 16 exp + 16 add + 8 cvt", 8, 56),
+]
+SPLIT_PROBE = 14
+
+
+def valu_rates():
+    """Issue rates of the softmax's instruction mix, in shader clocks per SIMD.
+
+    Each probe runs one instruction mix in a loop on every SIMD (one
+    workgroup per CU, ``w`` waves per SIMD) and every wave reads the shader
+    clock counter around its loop.  All waves of a SIMD run together, so the
+    SIMD's clocks per loop iteration are a wave's loop clocks / (iterations *
+    w); the split-roles probe does one block per pair of waves, and its SIMD
+    time is its slower role's.  The 100 MHz real-time counter read around the
+    same loops gives the shader clock the probe ran at.  Operands are nearly
+    constant, so the matrix cores run near the top clock here: these are issue
+    rates, not power-limited rates.
+    """
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "ring_attention_03_amd", "libattnprobe.so"))
+    lib.attn_probe_valu.restype = ctypes.c_int
+    lib.attn_probe_valu.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.empty(cus * 1024, device="cuda:0")
+    cyc = torch.empty(cus * 16, dtype=torch.int64, device="cuda:0")
+    rt = torch.empty(cus * 16, dtype=torch.int64, device="cuda:0")
+    rows = []
+    only = os.environ.get("VALU_PROBES")  # optional comma list of probe numbers
+    for mode, (name, n_mfma, n_valu) in enumerate(VALU_PROBES):
+        if only and str(mode) not in only.split(","):
+            continue
+        for w in ((2, 4) if mode == SPLIT_PROBE else (1, 2, 4)):
+            iters = 2000
+
+            def launch():
+                st = lib.attn_probe_valu(ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(cyc.data_ptr()),
+                                         ctypes.c_void_p(rt.data_ptr()), mode, cus, w, iters, stream)
+                if st != 0:
+                    raise RuntimeError(f"attn_probe_valu mode {mode} failed with HIP error {st}")
+            for _ in range(3):
+                launch()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            launch()
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e)
+            waves = cyc[: cus * 4 * w].double()
+            real = rt[: cus * 4 * w].double()
+            if mode == SPLIT_PROBE:
+                wave_cycles, blocks = float(waves.max()), iters * w / 2
+            else:
+                wave_cycles, blocks = float(waves.median()), iters * w
+            simd_per_iter = wave_cycles / blocks
+            # shader clock: counter ticks per second of the 100 MHz real-time counter
+            clock = float((waves / (real * 1e-8)).median()) / 1e9
+            row = {"probe": name, "waves_per_simd": w, "simd_clocks_per_iteration": round(simd_per_iter, 2),
+                   "clock_ghz": round(clock, 3), "launch_ms": round(ms, 4)}
+            if n_mfma == 0:
+                row["simd_clocks_per_vector_instruction"] = round(simd_per_iter / n_valu, 3)
+            elif n_valu == 0:
+                row["simd_clocks_per_mfma"] = round(simd_per_iter / n_mfma, 3)
+            else:
+                row["mfma_busy_if_32_clocks_each"] = round(32.0 * n_mfma / simd_per_iter, 3)
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    return rows
+
+
+def summarize_trace(folder, workload, warmup, steps):
+    """Attention-kernel durations of a rocprofv3 --kernel-trace run of this script.
+
+    Dispatches are taken in launch order.  A run launches warmup steps, then
+    the timed steps, then the same steps again with events around every
+    launch (cold passes are left out with --no-cold); the first
+    warmup * launches-per-step dispatches are the warmup and are listed apart.
+    """
+    import csv
+    import glob
+
+    from ring_attention_03_amd import RingLayout
+    from ring_attention_03_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[workload]
+    if w.mode != "ring" or w.rank is None:
+        raise SystemExit("--trace-from summarizes a single-rank ring workload")
+    lay = RingLayout(w.seqlens, w.n_chunks)
+    per_step = sum(1 for j in range(w.n_chunks) if j <= w.rank)  # chunks with visible keys
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if DOMINANT_KERNEL in r["Kernel_Name"]:
+                    rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    if len(rows) < per_step * (warmup + 2 * steps):
+        raise SystemExit(f"{len(rows)} dispatches, expected {per_step * (warmup + 2 * steps)}")
+    durs = [(e - s) * 1e-3 for s, e in rows]  # microseconds
+    warm, timed = durs[: per_step * warmup], durs[per_step * warmup:]
+    flops = 4 * w.head_dim * w.num_q_heads * lay.visible_pairs(w.rank) / per_step
+    avg = sum(timed) / len(timed)
+    rec = {"kernel": DOMINANT_KERNEL, "workload": workload, "kernel_source_sha": kernel_source_hash(),
+           "launches_per_step": per_step, "warmup_dispatches": len(warm),
+           "warmup_avg_us": sum(warm) / len(warm) if warm else None,
+           "timed_dispatches": len(timed), "timed_avg_us": avg, "timed_min_us": min(timed),
+           "timed_max_us": max(timed), "kernel_ms_per_step": avg * per_step * 1e-3,
+           "flop_per_launch": flops, "achieved_tflops": flops / (avg * 1e-6) / 1e12}
+    print(json.dumps(rec, indent=1), flush=True)
+
+
 def main():
     args = parse_args()
+    if args.trace_from:
+        summarize_trace(args.trace_from, args.workload, args.warmup, args.steps)
+        return
     if args.counters_from:
         summarize_counters(args.counters_from)
         return
@@ -529,6 +694,9 @@ def main():
     if args.mfma_ceiling:
         mfma_ceiling()
         return
+    if args.valu_rates:
+        valu_rates()
+        return
     from ring_attention_03_amd import load_library
 
     load_library()
@@ -539,7 +707,8 @@ def main():
     wall, per_kind = time_job(job, args.steps, args.warmup)
     main_res = summarize(job, args.steps, wall, per_kind)
     # the same step with L2 and MALL flushed before it (median of 11)
-    main_res["cold_ms_per_step_median"] = time_cold(job, 11)
+    if not args.no_cold:
+        main_res["cold_ms_per_step_median"] = time_cold(job, 11)
     log(f"bench: {args.workload}: {main_res['ms_per_step']:.3f} ms/step, {main_res['tflops']:.1f} TFLOP/s "
         f"({main_res['pct_bf16_peak']:.1f}% of bf16 peak)")
 

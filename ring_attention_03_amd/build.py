@@ -20,9 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattnring.so")
 SOURCES = ["fwd_bf16.hip", "fwd_f32.hip", "merge.hip", "abi.cpp"]
-# matrix-core rate probe used by bench.py --mfma-ceiling; not part of the attention ABI
+# matrix-core and vector-ALU rate probes (bench.py --mfma-ceiling, --valu-rates); not part of the attention ABI
 PROBE_LIB = os.path.join(PKG, "libattnprobe.so")
-PROBE_SOURCES = ["probe_mfma.hip"]
+PROBE_SOURCES = ["probe_mfma.hip", "probe_valu.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

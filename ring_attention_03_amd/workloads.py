@@ -74,6 +74,9 @@ WORKLOADS = {
     "ring_100k_n16": Workload(
         "ring_100k_n16", (102400,), 16, None, 64, 8, 64, "bf16", "normal", 4, "ring",
         "S=102400 in 16 ring chunks of 6400, every rank"),
+    "ring_100k_n16_rank15": Workload(
+        "ring_100k_n16_rank15", (102400,), 16, 15, 64, 8, 64, "bf16", "normal", 4, "ring",
+        "S=102400 in 16 ring chunks of 6400, last rank (heaviest causal share)"),
     "ring_64k_zigzag_rank7": Workload(
         "ring_64k_zigzag_rank7", (65536,), 8, 7, 64, 8, 64, "bf16", "uniform", 3, "zigzag",
         "S=65536 on 8 devices, load-balanced: 16 chunks of 4096, rank 7 holds chunks 7 and 8"),
