@@ -13,7 +13,10 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnring.so")
+# the in-tree build; ATTNRING_LIB may name another build of the same ABI (the
+# tests point it at an AddressSanitizer build of the host code)
+LIB_PATH = os.environ.get("ATTNRING_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libattnring.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_DTYPE_BF16, ATTN_DTYPE_FP32 = 0, 1
