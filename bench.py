@@ -542,7 +542,7 @@ VALU_PROBES = [
     ("mfma_with_fma: 8 mfma + 32 fma", 8, 32),
     ("mfma_with_exp: 8 mfma + 16 exp", 8, 16),
     ("mfma_with_fma64: 8 mfma + 64 fma", 8, 64),
-    ("split_roles: 8 mfma in one wave, 16 fma + 16 exp + 16 add + 8 cvt in another, per SIMD", 8, 56),
+    None,  # (probe 14 retired)
     ("block_mix_poly_exp: 8 mfma + 16 fma + 16 cubic exp2 + 16 add + 8 cvt", 8, 168),
     ("block_mix_16x16x32: 16 mfma 16x16x32 + 16 fma + 16 exp + 16 add + 8 cvt", 8, 56),
     ("mfma_agpr_with_fma: 8 mfma (AGPR accumulators) + 32 fma", 8, 32),
@@ -551,22 +551,27 @@ VALU_PROBES = [
     ("mfma_ab_agpr_with_fma: 8 mfma (A, B, C in AGPRs) + 32 fma", 8, 32),
     ("block_mix_ab_agpr: 8 mfma (A, B, C in AGPRs) + 16 fma + 16 exp + 16 add + 8 cvt", 8, 56),
     ("block_mix_a_agpr: 8 mfma (A, C in AGPRs) + 16 fma + 16 exp + 16 add + 8 cvt", 8, 56),
+    ("block_mix_lds: the block mix with A operands from 4 ds_read_b128 + 8 ds_read_b64_tr_b16", 8, 56),
+    ("block_mix_lds_unused: the same LDS reads issued, MFMAs on register operands", 8, 56),
+    ("block_mix_lds_b128: the value operands by 4 ds_read_b128 (same bytes, 8 reads per block)", 8, 56),
+    ("block_mix_lds_2tiles: two query sub-tiles per wave share each read (per-block figures)", 16, 112),
 ]
-SPLIT_PROBE = 14
+
 
 
 def valu_rates():
     """Issue rates of the softmax's instruction mix, in shader clocks per SIMD.
 
-    Each probe runs one instruction mix in a loop on every SIMD (one
-    workgroup per CU, ``w`` waves per SIMD) and every wave reads the shader
-    clock counter around its loop.  All waves of a SIMD run together, so the
-    SIMD's clocks per loop iteration are a wave's loop clocks / (iterations *
-    w); the split-roles probe does one block per pair of waves, and its SIMD
-    time is its slower role's.  The 100 MHz real-time counter read around the
-    same loops gives the shader clock the probe ran at.  Operands are nearly
-    constant, so the matrix cores run near the top clock here: these are issue
-    rates, not power-limited rates.
+    Each probe runs one instruction mix in a loop on every SIMD with w = 1, 2
+    or 4 waves per SIMD (one workgroup of 4*w waves per CU).  Every wave reads
+    the shader-clock counter (s_memtime) and the 100 MHz real-time counter
+    around its loop and records its start; the waves of a workgroup start
+    together (the start spread is reported).  Waves sharing a SIMD do not
+    progress evenly - the oldest issues first - so a SIMD's time is its
+    slowest wave's: SIMD clocks per loop iteration = the longest loop of a
+    workgroup / (iterations * w), the median over workgroups.  Operands are
+    nearly constant, so the clock stays high: these are issue rates, not
+    power-limited rates.
     """
     import ctypes
 
@@ -574,26 +579,25 @@ def valu_rates():
 
     lib = ctypes.CDLL(os.path.join(ROOT, "ring_attention_03_amd", "libattnprobe.so"))
     lib.attn_probe_valu.restype = ctypes.c_int
-    lib.attn_probe_valu.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_probe_valu.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    sink = torch.empty(cus * 1024, device="cuda:0")
-    cyc = torch.empty(cus * 16, dtype=torch.int64, device="cuda:0")
-    rt = torch.empty(cus * 16, dtype=torch.int64, device="cuda:0")
+    sink = torch.empty(cus * 4 * 256, device="cuda:0")
+    cyc, rt, st0 = (torch.empty(cus * 16, dtype=torch.int64, device="cuda:0") for _ in range(3))
     rows = []
     only = os.environ.get("VALU_PROBES")  # optional comma list of probe numbers
-    for mode, (name, n_mfma, n_valu) in enumerate(VALU_PROBES):
-        if only and str(mode) not in only.split(","):
+    for mode, probe in enumerate(VALU_PROBES):
+        if probe is None or (only and str(mode) not in only.split(",")):
             continue
-        for w in ((2, 4) if mode == SPLIT_PROBE else (1, 2, 4)):
+        name, n_mfma, n_valu = probe
+        for w in (1, 2, 4):
             iters = 2000
 
             def launch():
-                st = lib.attn_probe_valu(ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(cyc.data_ptr()),
-                                         ctypes.c_void_p(rt.data_ptr()), mode, cus, w, iters, stream)
-                if st != 0:
-                    raise RuntimeError(f"attn_probe_valu mode {mode} failed with HIP error {st}")
+                rc = lib.attn_probe_valu(*(ctypes.c_void_p(t.data_ptr()) for t in (sink, cyc, rt, st0)),
+                                         mode, cus, w, iters, stream)
+                if rc != 0:
+                    raise RuntimeError(f"attn_probe_valu mode {mode} failed with HIP error {rc}")
             for _ in range(3):
                 launch()
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -602,67 +606,23 @@ def valu_rates():
             e.record()
             torch.cuda.synchronize()
             ms = s.elapsed_time(e)
-            waves = cyc[: cus * 4 * w].double()
-            real = rt[: cus * 4 * w].double()
-            if mode == SPLIT_PROBE:
-                wave_cycles, blocks = float(waves.max()), iters * w / 2
-            else:
-                wave_cycles, blocks = float(waves.median()), iters * w
-            simd_per_iter = wave_cycles / blocks
-            # shader clock: counter ticks per second of the 100 MHz real-time counter
-            clock = float((waves / (real * 1e-8)).median()) / 1e9
+            n = cus * 4 * w
+            ticks, real, start = cyc[:n].double(), rt[:n].double(), st0[:n].double()
+            simd_per_iter = float(ticks.view(cus, 4 * w).max(dim=1).values.median()) / (iters * w)
+            clock = float((ticks / (real * 1e-8)).median()) / 1e9
+            spread = float((start.max() - start.min()) / real.median())
             row = {"probe": name, "waves_per_simd": w, "simd_clocks_per_iteration": round(simd_per_iter, 2),
-                   "clock_ghz": round(clock, 3), "launch_ms": round(ms, 4)}
+                   "clock_ghz": round(clock, 3), "launch_ms": round(ms, 4),
+                   "start_spread_of_loop": round(spread, 4)}
             if n_mfma == 0:
                 row["simd_clocks_per_vector_instruction"] = round(simd_per_iter / n_valu, 3)
             elif n_valu == 0:
                 row["simd_clocks_per_mfma"] = round(simd_per_iter / n_mfma, 3)
             else:
-                row["mfma_busy_if_32_clocks_each"] = round(32.0 * n_mfma / simd_per_iter, 3)
+                row["mfma_busy"] = round(32.0 * n_mfma / simd_per_iter, 3)
             rows.append(row)
             print(json.dumps(row), flush=True)
     return rows
-
-
-def summarize_trace(folder, workload, warmup, steps):
-    """Attention-kernel durations of a rocprofv3 --kernel-trace run of this script.
-
-    Dispatches are taken in launch order.  A run launches warmup steps, then
-    the timed steps, then the same steps again with events around every
-    launch (cold passes are left out with --no-cold); the first
-    warmup * launches-per-step dispatches are the warmup and are listed apart.
-    """
-    import csv
-    import glob
-
-    from ring_attention_03_amd import RingLayout
-    from ring_attention_03_amd.workloads import WORKLOADS
-
-    w = WORKLOADS[workload]
-    if w.mode != "ring" or w.rank is None:
-        raise SystemExit("--trace-from summarizes a single-rank ring workload")
-    lay = RingLayout(w.seqlens, w.n_chunks)
-    per_step = sum(1 for j in range(w.n_chunks) if j <= w.rank)  # chunks with visible keys
-    rows = []
-    for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
-        with open(path, newline="") as f:
-            for r in csv.DictReader(f):
-                if DOMINANT_KERNEL in r["Kernel_Name"]:
-                    rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
-    rows.sort()
-    if len(rows) < per_step * (warmup + 2 * steps):
-        raise SystemExit(f"{len(rows)} dispatches, expected {per_step * (warmup + 2 * steps)}")
-    durs = [(e - s) * 1e-3 for s, e in rows]  # microseconds
-    warm, timed = durs[: per_step * warmup], durs[per_step * warmup:]
-    flops = 4 * w.head_dim * w.num_q_heads * lay.visible_pairs(w.rank) / per_step
-    avg = sum(timed) / len(timed)
-    rec = {"kernel": DOMINANT_KERNEL, "workload": workload, "kernel_source_sha": kernel_source_hash(),
-           "launches_per_step": per_step, "warmup_dispatches": len(warm),
-           "warmup_avg_us": sum(warm) / len(warm) if warm else None,
-           "timed_dispatches": len(timed), "timed_avg_us": avg, "timed_min_us": min(timed),
-           "timed_max_us": max(timed), "kernel_ms_per_step": avg * per_step * 1e-3,
-           "flop_per_launch": flops, "achieved_tflops": flops / (avg * 1e-6) / 1e12}
-    print(json.dumps(rec, indent=1), flush=True)
 
 
 def main():

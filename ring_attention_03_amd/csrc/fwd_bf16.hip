@@ -518,7 +518,7 @@ void fwd_bf16_kernel(FwdParams p) {
   // the running state (o, lse) by their log-sum-exps (rows that saw no key here
   // leave the state as it is)
   const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
   // (the lane index is taken afresh from the exec mask, so no lane-derived value
   // has to stay live across the loop)
   const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -543,20 +543,25 @@ void fwd_bf16_kernel(FwdParams p) {
         }
       if (half_e == 0) *lse_dst = lse_b;
     } else if (l_tot > 0.f) {
+      // the running state's O and LSE are loaded together, before the weights
+      // need the LSE (both halves read the LSE before half 0 writes it)
+      f32x4 oa[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) oa[k] = *reinterpret_cast<const f32x4*>(dst + (k >> 2) * 32 + (k & 3) * 8);
+      const float la = *lse_dst;
       float lse, wa, wb;
-      lse_merge_weights(*lse_dst, lse_b, &lse, &wa, &wb);  // both halves read before half 0 writes
+      lse_merge_weights(la, lse_b, &lse, &wa, &wb);
+      const float wbi = wb * inv;  // this block's weight times its normaliser
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 ob;
-          ob[0] = acc[db][i * 4 + 0] * inv;
-          ob[1] = acc[db][i * 4 + 1] * inv;
-          ob[2] = acc[db][i * 4 + 2] * inv;
-          ob[3] = acc[db][i * 4 + 3] * inv;
-          f32x4* o4 = reinterpret_cast<f32x4*>(dst + db * 32 + i * 8);
-          *o4 = wa * *o4 + wb * ob;
-        }
+      for (int k = 0; k < 8; ++k) {
+        const int db = k >> 2, i = k & 3;
+        f32x4 o4;
+        o4[0] = fmaf(wbi, acc[db][i * 4 + 0], wa * oa[k][0]);
+        o4[1] = fmaf(wbi, acc[db][i * 4 + 1], wa * oa[k][1]);
+        o4[2] = fmaf(wbi, acc[db][i * 4 + 2], wa * oa[k][2]);
+        o4[3] = fmaf(wbi, acc[db][i * 4 + 3], wa * oa[k][3]);
+        *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = o4;
+      }
       if (half_e == 0) *lse_dst = lse;
     }
   }

@@ -3,12 +3,14 @@
 //
 // At head_dim 64 every score costs 256 matrix-core flops and about four vector
 // instructions (scale-and-shift FMA, base-2 exponential, row-sum add, half a
-// bf16 pack), so how fast the vector ALU issues those, and how much of it hides
-// under the matrix core, bounds the kernel.  Each probe runs one instruction
-// mix in a loop on every SIMD of the chip, `waves` waves per SIMD (one
-// workgroup of 4*waves waves per CU), and every wave records the shader-clock
-// cycles (s_memtime) its loop took.  The host divides by the instruction
-// counts to get SIMD clocks per wave-instruction.
+// bf16 pack), and the MFMA operands come from LDS; how fast a SIMD issues that
+// mix bounds the kernel.  Each probe runs one instruction mix in a loop on
+// every SIMD of the chip with w waves per SIMD: one workgroup of 4*w waves
+// per CU (its 84 KiB of LDS keeps any other workgroup off the CU).  Every wave
+// records the shader-clock cycles (s_memtime) its loop took, the real-time
+// counter's ticks over the same loop and its start.  Waves sharing a SIMD do
+// not progress evenly (the oldest issues first), so the host takes a SIMD's
+// time as its slowest wave's.
 //
 // Probes (mode):
 //   0 fma     v_fma_f32             8 independent chains
@@ -26,8 +28,7 @@
 //  11 mfma+fma  8 MFMA 32x32x16 + 32 independent FMAs, interleaved
 //  12 mfma+exp  8 MFMA 32x32x16 + 16 independent exponentials, interleaved
 //  13 mfma+fma64  8 MFMA 32x32x16 + 64 independent FMAs, interleaved
-//  14 split     waves 0-3 of every 8 run 8 MFMAs per iteration, waves 4-7 the
-//               vector part of the block mix (the two roles share each SIMD)
+//  14 (retired)
 //  15 mix_poly  the block mix with every exponential computed by a cubic
 //               polynomial on the FMA unit instead of v_exp_f32
 //  16 mix16     the block mix with the matrix work as 16 v_mfma_f32_16x16x32_bf16
@@ -37,7 +38,15 @@
 //  20 mfma_ab_agpr+fma  8 MFMA 32x32x16 with A, B and C in AGPRs + 32 FMAs
 //  21 mix_ab_agpr  the block mix with the MFMAs' A, B and C in AGPRs
 //  22 mix_a_agpr   the block mix with A and C in AGPRs, B in VGPRs
-// Every wave also reads the real-time counter around its loop.
+//  23 mix_lds      the block mix with the attention kernel's LDS reads: the
+//                  MFMAs' A operands come from 4 ds_read_b128 and 8
+//                  ds_read_b64_tr_b16 per iteration, as in the kernel
+//  24 mix_lds_free the same reads issued, but the MFMAs use register operands
+//                  (the reads' results are only kept alive)
+//  25 mix_lds_b128 as 23, with the value operands read by 4 ds_read_b128
+//                  (the same bytes in 8 instead of 12 reads)
+//  26 mix_lds_2tile two query sub-tiles per wave share every LDS operand:
+//                  per iteration 16 MFMAs, twice the vector work, 12 reads
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -214,11 +223,79 @@ __device__ __forceinline__ float mix_probe(int iters) {
   return t;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// The block mix fed from LDS like the attention kernel: per iteration 4 A
+// operands by ds_read_b128 (keys) and 8 half-operands by ds_read_b64_tr_b16
+// (values), addresses inside the 16 KiB at `lds`.
+template <bool FEED, bool VB128 = false, int TILES = 1>
+__device__ __forceinline__ float mix_lds_probe(int iters, const __attribute__((address_space(3))) char* lds) {
+  bf16x8 r1, r2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    r1[j] = (__bf16)lane_value(j + 8);
+    r2[j] = (__bf16)lane_value(j + 9);
+  }
+  const int lane = __builtin_amdgcn_workitem_id_x() & 63;
+  // lane-linear addresses: conflict-free, like the kernel's swizzled tile reads
+  const int ka = lane * 16;
+  const int va = lane * 8;
+  f32x16 c[2 * TILES] = {};
+  float s[16], e[16], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s[j] = lane_value(j + 20);
+  unsigned pk[8];
+  const float cs = lane_value(50), nm = -lane_value(51), nm2 = -lane_value(52);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(s[j]));
+    bf16x8 kop[4], vop[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      kop[k] = *(const __attribute__((address_space(3))) bf16x8*)(lds + ka + k * 1024 + (it & 1) * 4096);
+      if constexpr (VB128) {
+        vop[k] = *(const __attribute__((address_space(3))) bf16x8*)(lds + 8192 + ka + k * 1024);
+      } else {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + 8192 + va + k * 1024));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + 8192 + va + k * 1024 + 512));
+        vop[k] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8 * TILES; ++k) {
+      const int kk = k % 8, tl = k / 8;
+      const bf16x8 a = kk < 4 ? vop[kk] : kop[kk - 4];
+      if constexpr (FEED) {
+        c[(k & 1) + 2 * tl] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, tl ? r2 : r1, c[(k & 1) + 2 * tl], 0, 0, 0);
+      } else {
+        asm volatile("" ::"v"(a));
+        c[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1, r1, c[k & 1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = 2 * kk + j;
+        e[i] = __builtin_amdgcn_exp2f(fmaf(s[i], cs, tl ? nm2 : nm));
+        acc[i & 3] += e[i];
+      }
+      const bf16x2 p2 = {(__bf16)e[2 * kk], (__bf16)e[2 * kk + 1]};
+      pk[kk] = __builtin_bit_cast(unsigned, p2);
+      asm volatile("" ::"v"(pk[kk]));
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+  }
+  float t = acc[0] + acc[1] + acc[2] + acc[3] + c[0][0] + c[1][5] + c[2 * TILES - 1][3];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t += s[j];
+  return t;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(1024) void probe_valu_kernel(float* sink, unsigned long long* cycles,
-                                                          unsigned long long* realtime, int iters) {
-  // 84 KiB of LDS per workgroup: at most one workgroup per CU (160 KiB), so
-  // every SIMD runs exactly the requested number of waves
+                                                          unsigned long long* realtime, unsigned long long* starts,
+                                                          int iters) {
   __shared__ float pad[84 * 256];
   const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
@@ -227,12 +304,18 @@ __global__ __launch_bounds__(1024) void probe_valu_kernel(float* sink, unsigned 
     r = vector_probe<MODE>(iters);
   } else if constexpr (MODE <= 7) {
     r = matrix_probe<MODE>(iters);
-  } else if constexpr (MODE == 14) {
-    // role by wave index: waves w and w+4 share a SIMD
-    if (((__builtin_amdgcn_workitem_id_x() >> 8) & 1) == 0)
-      r = matrix_probe<6>(iters / 2);  // 16 MFMAs per iteration: 8 per block-iteration
+  } else if constexpr (MODE >= 23 && MODE <= 26) {
+    // 16 KiB of this workgroup's LDS as the operand source (contents arbitrary but finite)
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    for (int i = tid; i < 4096; i += __builtin_amdgcn_workgroup_size_x()) pad[i] = 0.001f * (float)(i & 255);
+    __syncthreads();
+    const auto* lds = (const __attribute__((address_space(3))) char*)(const __attribute__((address_space(3))) float*)pad;
+    if constexpr (MODE == 25)
+      r = mix_lds_probe<true, true>(iters, lds);
+    else if constexpr (MODE == 26)
+      r = mix_lds_probe<true, false, 2>(iters, lds);
     else
-      r = mix_probe<10>(iters);
+      r = mix_lds_probe<MODE == 23>(iters, lds);
   } else {
     r = mix_probe<MODE>(iters);
   }
@@ -246,13 +329,14 @@ __global__ __launch_bounds__(1024) void probe_valu_kernel(float* sink, unsigned 
   if ((tid & 63) == 0) {
     cycles[gid >> 6] = t1 - t0;
     realtime[gid >> 6] = r1 - r0;
+    starts[gid >> 6] = r0;
   }
 }
 
 template <int MODE>
-hipError_t launch(float* sink, unsigned long long* cycles, unsigned long long* realtime, int blocks, int threads,
-                  int iters, hipStream_t s) {
-  hipLaunchKernelGGL(probe_valu_kernel<MODE>, dim3(blocks), dim3(threads), 0, s, sink, cycles, realtime, iters);
+hipError_t launch(float* sink, unsigned long long* cycles, unsigned long long* realtime, unsigned long long* starts,
+                  int cus, int w, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(probe_valu_kernel<MODE>, dim3(cus), dim3(256 * w), 0, s, sink, cycles, realtime, starts, iters);
   return hipGetLastError();
 }
 
@@ -260,47 +344,50 @@ hipError_t launch(float* sink, unsigned long long* cycles, unsigned long long* r
 
 // Instructions of each probe per loop iteration (per wave), for the host's arithmetic:
 // vector probes 32 (4 unrolled x 8 chains); matrix probes 16 MFMAs; mix probes one block.
-extern "C" int attn_probe_valu_modes(void) { return 23; }
+extern "C" int attn_probe_valu_modes(void) { return 27; }
 
-// Run probe `mode` with `blocks` workgroups of 64*4*waves_per_simd threads for
-// `iters` iterations.  `sink` must hold blocks*threads floats, `cycles` and
-// `realtime` blocks*threads/64 counters each (one per wave: its loop's
-// s_memtime and s_memrealtime deltas).
+// Run probe `mode` on `cus` CUs with `waves_per_simd` (1, 2 or 4) waves per
+// SIMD for `iters` iterations: cus workgroups of 256 * waves_per_simd threads.
+// `sink` must hold cus*waves_per_simd*256 floats; `cycles`, `realtime` and
+// `starts` cus*waves_per_simd*4 counters each (one per wave: its loop's
+// s_memtime and s_memrealtime deltas, and its start on the real-time counter).
 // Returns 0 or a HIP error code (invalid arguments: hipErrorInvalidValue,
 // nothing launched).
-extern "C" int attn_probe_valu(float* sink, unsigned long long* cycles, unsigned long long* realtime, int mode,
-                               int blocks, int waves_per_simd, int iters, hipStream_t stream) {
-  if (!sink || !cycles || !realtime || blocks < 1 || iters < 1 || waves_per_simd < 1 || waves_per_simd > 4)
+extern "C" int attn_probe_valu(float* sink, unsigned long long* cycles, unsigned long long* realtime,
+                               unsigned long long* starts, int mode, int cus, int waves_per_simd, int iters,
+                               hipStream_t stream) {
+  if (!sink || !cycles || !realtime || !starts || cus < 1 || iters < 1 ||
+      (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4) || mode == 14)
     return (int)hipErrorInvalidValue;
-  const int threads = 64 * 4 * waves_per_simd;
+  const int w = waves_per_simd;
   hipError_t e;
   switch (mode) {
-    case 0: e = launch<0>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 1: e = launch<1>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 2: e = launch<2>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 3: e = launch<3>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 4: e = launch<4>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 5: e = launch<5>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 6: e = launch<6>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 7: e = launch<7>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 8: e = launch<8>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 9: e = launch<9>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 10: e = launch<10>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 11: e = launch<11>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 12: e = launch<12>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 13: e = launch<13>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 14:
-      if (waves_per_simd < 2) return (int)hipErrorInvalidValue;  // two roles per SIMD
-      e = launch<14>(sink, cycles, realtime, blocks, threads, iters, stream);
-      break;
-    case 15: e = launch<15>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 16: e = launch<16>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 17: e = launch<17>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 18: e = launch<18>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 19: e = launch<19>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 20: e = launch<20>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 21: e = launch<21>(sink, cycles, realtime, blocks, threads, iters, stream); break;
-    case 22: e = launch<22>(sink, cycles, realtime, blocks, threads, iters, stream); break;
+    case 0: e = launch<0>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 1: e = launch<1>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 2: e = launch<2>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 3: e = launch<3>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 4: e = launch<4>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 5: e = launch<5>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 6: e = launch<6>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 7: e = launch<7>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 8: e = launch<8>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 9: e = launch<9>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 10: e = launch<10>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 11: e = launch<11>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 12: e = launch<12>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 13: e = launch<13>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 15: e = launch<15>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 16: e = launch<16>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 17: e = launch<17>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 18: e = launch<18>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 19: e = launch<19>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 20: e = launch<20>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 21: e = launch<21>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 22: e = launch<22>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 23: e = launch<23>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 24: e = launch<24>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 25: e = launch<25>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 26: e = launch<26>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)e;
