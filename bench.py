@@ -625,6 +625,47 @@ def valu_rates():
     return rows
 
 
+def summarize_trace(folder, workload, warmup, steps):
+    """Attention-kernel durations of a rocprofv3 --kernel-trace run of this script.
+
+    Dispatches are taken in launch order.  A run launches warmup steps, then
+    the timed steps, then the same steps again with events around every
+    launch (cold passes are left out with --no-cold); the first
+    warmup * launches-per-step dispatches are the warmup and are listed apart.
+    """
+    import csv
+    import glob
+
+    from ring_attention_03_amd import RingLayout
+    from ring_attention_03_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[workload]
+    if w.mode != "ring" or w.rank is None:
+        raise SystemExit("--trace-from summarizes a single-rank ring workload")
+    lay = RingLayout(w.seqlens, w.n_chunks)
+    per_step = sum(1 for j in range(w.n_chunks) if j <= w.rank)  # chunks with visible keys
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if DOMINANT_KERNEL in r["Kernel_Name"]:
+                    rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    if len(rows) < per_step * (warmup + 2 * steps):
+        raise SystemExit(f"{len(rows)} dispatches, expected {per_step * (warmup + 2 * steps)}")
+    durs = [(e - s) * 1e-3 for s, e in rows]  # microseconds
+    warm, timed = durs[: per_step * warmup], durs[per_step * warmup:]
+    flops = 4 * w.head_dim * w.num_q_heads * lay.visible_pairs(w.rank) / per_step
+    avg = sum(timed) / len(timed)
+    rec = {"kernel": DOMINANT_KERNEL, "workload": workload, "kernel_source_sha": kernel_source_hash(),
+           "launches_per_step": per_step, "warmup_dispatches": len(warm),
+           "warmup_avg_us": sum(warm) / len(warm) if warm else None,
+           "timed_dispatches": len(timed), "timed_avg_us": avg, "timed_min_us": min(timed),
+           "timed_max_us": max(timed), "kernel_ms_per_step": avg * per_step * 1e-3,
+           "flop_per_launch": flops, "achieved_tflops": flops / (avg * 1e-6) / 1e12}
+    print(json.dumps(rec, indent=1), flush=True)
+
+
 def main():
     args = parse_args()
     if args.trace_from:

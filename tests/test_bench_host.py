@@ -98,3 +98,32 @@ def test_counter_summary_clock_and_busy(tmp_path, capsys):
     assert abs(rec["mfma_busy_pct"] - 50.0) < 1e-9
     assert abs(rec["valu_per_mfma"] - 8.5) < 1e-12 and abs(rec["lds_per_mfma"] - 1.5) < 1e-12
     assert abs(rec["lds_active_pct"] - 25.0) < 1e-9 and rec["lds_bank_conflict_pct"] == 0.0
+
+
+def test_trace_summary_lists_the_warmup_apart(tmp_path, capsys):
+    """--trace-from: dispatches in launch order, the first warmup x launches-per-step are the
+    warmup; the rest (timed pass and event-timed pass) give the average launch."""
+    bench = _load_bench()
+    folder = tmp_path / "kt"
+    folder.mkdir()
+    per_step, warmup, steps = 8, 2, 3     # ring_64k_rank7: 8 active chunks per ring pass
+    durs = [2000.0] * (per_step * warmup) + [1000.0, 500.0] * (per_step * steps)  # microseconds
+    with open(folder / "kt_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        t = 10_000
+        rows = []
+        for i, d in enumerate(durs):
+            rows.append([i, "attnring::fwd_bf16_kernel<8>", t, t + int(d * 1e3)])
+            t += int(d * 1e3) + 50
+        for r in reversed(rows):              # file order must not matter: sorted by start
+            w.writerow(r)
+        w.writerow([999, "other_kernel", 0, 5])
+    bench.summarize_trace(str(folder), "ring_64k_rank7", warmup, steps)
+    rec = json.loads(capsys.readouterr().out)
+    assert rec["launches_per_step"] == per_step
+    assert rec["warmup_dispatches"] == per_step * warmup and rec["warmup_avg_us"] == 2000.0
+    assert rec["timed_dispatches"] == 2 * per_step * steps and rec["timed_avg_us"] == 750.0
+    assert abs(rec["kernel_ms_per_step"] - 6.0) < 1e-12
+    flop = 4 * 64 * 64 * (lambda c: sum(range(7 * c + 1, 8 * c + 1)))(8192) / per_step
+    assert rec["flop_per_launch"] == flop
