@@ -555,6 +555,9 @@ VALU_PROBES = [
     ("block_mix_lds_unused: the same LDS reads issued, MFMAs on register operands", 8, 56),
     ("block_mix_lds_b128: the value operands by 4 ds_read_b128 (same bytes, 8 reads per block)", 8, 56),
     ("block_mix_lds_2tiles: two query sub-tiles per wave share each read (per-block figures)", 16, 112),
+    ("v_mul_f32", 0, 32), ("v_fmamk_f32 (literal multiplier)", 0, 32), ("v_fmac_f32", 0, 32),
+    ("block_mix_literal_scale: the block mix with its FMAs as v_fmamk_f32", 8, 56),
+    ("block_mix_lds_literal_scale: the LDS-fed block mix with its FMAs as v_fmamk_f32", 8, 56),
 ]
 
 

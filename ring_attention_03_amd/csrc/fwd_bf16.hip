@@ -9,23 +9,26 @@
 // log-sum-exp.  The same kernel run over a whole sequence is full causal
 // prefill.
 //
-// Work decomposition.  A workgroup of 8 waves owns (sequence, row tile, group
-// of query heads that share one key/value head); each wave owns 32 query rows
-// of one head, kept in registers.  Key/value tiles of 128 keys are copied from
-// HBM straight into LDS (global_load_lds, no register staging) and read by all
-// 8 waves, so a tile is shared by every query head of its GQA group.  A wave
-// needs at most 128 VGPRs, so two workgroups - four waves per SIMD - share a
-// CU.
+// Work decomposition.  A workgroup of 4 waves owns (sequence, row tile, group
+// of query heads that share one key/value head); each wave owns 64 query rows
+// of one head, kept in registers as two 32-row sub-tiles.  Key/value tiles of
+// 128 keys are copied from HBM straight into LDS (global_load_lds, no register
+// staging) and read by all 4 waves, so a tile is shared by the query heads of
+// the group.  Every key or value operand a wave reads from LDS feeds the
+// MFMAs of both sub-tiles: per score, half the LDS bytes of a 32-row wave, and
+// two independent dependency chains per wave.  A wave needs up to 256 VGPRs,
+// so two workgroups - two waves per SIMD, one of each - share a CU.
 //
 // Software pipeline.  Each wave walks its key range in 32-key blocks; the
 // softmax of block i (vector ALU) is interleaved with O += P V of block i-1
-// and S = K Q^T of block i+1 (matrix cores), which do not depend on it, so a
-// single wave keeps both units busy and the other resident waves fill the
-// gaps.  Keys of block i are read from LDS one step before its softmax and
-// values at the end of it (held in registers for the next step's O += P V),
-// so values live one tile longer than keys: LDS holds two key buffers and
-// three value buffers (80 KiB), and one barrier per tile separates the copy of
-// tile t+2 from the last reads of the buffers it reuses.
+// and S = K Q^T of block i+1 (matrix cores), which do not depend on it: the
+// first half of a step exponentiates sub-tile 0 beside O += P V of both
+// sub-tiles, the second half sub-tile 1 beside S = K Q^T of both.  Keys of
+// block i+1 are read from LDS at the start of the second half and values of
+// block i at the end of the step (held in registers for the next step's
+// O += P V), so values live one tile longer than keys: LDS holds two key
+// buffers and three value buffers (80 KiB), and one barrier per tile separates
+// the copy of tile t+2 from the last reads of the buffers it reuses.
 //
 // Register layouts (v_mfma_f32_32x32x16_bf16: A is 32x16, B is 16x32, lane l
 // supplies row/col l%32 and k-slots 8*(l/32)..+7; D lane l holds column l%32,
@@ -58,17 +61,16 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned short lds_u16;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void global_cvoid;
 
 constexpr int D = kHeadDim;       // 64
-constexpr int NW = kBf16Waves;    // waves per workgroup (8)
-constexpr int QW = kBf16RowsPerWave;  // query rows per wave (32)
+constexpr int NW = kBf16Waves;    // waves per workgroup (4)
+constexpr int QW = kBf16RowsPerWave;  // query rows per wave (64)
+constexpr int SUB = QW / 32;      // 32-row sub-tiles per wave (2)
+static_assert(SUB == 2, "a step exponentiates one sub-tile in each half");
 constexpr int BT = 128;           // keys per LDS tile
 constexpr int BPT = BT / 32;      // 32-key blocks per tile
 
@@ -90,10 +92,6 @@ __device__ __forceinline__ int v_pos(int key, int chunk) { return chunk ^ ((key 
 __device__ __forceinline__ int k_off(int key, int chunk) { return key * D + (k_pos(key, chunk) << 3); }
 __device__ __forceinline__ int v_off(int key, int chunk) { return key * D + (v_pos(key, chunk) << 3); }
 
-template <bool B>
-struct MaskTag {
-  static constexpr bool value = B;
-};
 template <int V>
 struct Int {
   static constexpr int value = V;
@@ -136,7 +134,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 template <int HPW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdParams p) {
   // LDS: NKB key tile buffers, then NVB value tile buffers (16 KiB each)
   __shared__ __attribute__((aligned(16))) unsigned short lds[(NKB + NVB) * TILE_ELEMS];
@@ -153,8 +151,13 @@ void fwd_bf16_kernel(FwdParams p) {
   // ---- which (sequence, row tile, head group) this workgroup owns
   // (the division runs on the vector unit; readfirstlane keeps everything derived
   // from it in scalar registers)
-  const int unit = __builtin_amdgcn_readfirstlane(wg / p.n_head_groups);
-  const int hg = wg - unit * p.n_head_groups;
+  const int G = p.n_head_groups;
+  const int unit = __builtin_amdgcn_readfirstlane(wg / G);
+  int hg = wg - unit * G;
+  // workgroup w runs on XCD w % 8: when the groups divide evenly, XCD x takes a
+  // contiguous range of head groups, so groups that share a key/value head
+  // also share that XCD's L2
+  if ((G & 7) == 0) hg = (hg & 7) * (G >> 3) + (hg >> 3);
   int s = 0;
   while (unit >= p.unit_off[s + 1]) ++s;
   const int tile = (p.unit_off[s + 1] - 1) - unit;  // heaviest (last) row tile first
@@ -179,15 +182,17 @@ void fwd_bf16_kernel(FwdParams p) {
   // blocks [0, nfull) are visible to every row of the tile; later ones need the mask
   const int nfull = min(nblk, kfull >> 5);
 
-  // ---- this wave's queries as MFMA B operands: qr[ks] = q[row][16*ks + 8*half .. +7]
-  bf16x8 qr[4];
-  {
-    const int row = rw0 + l32;
+  // ---- this wave's queries as MFMA B operands, per sub-tile sb (rows rw0 + 32*sb ..):
+  // qr[sb][ks] = q[row][16*ks + 8*half .. +7]
+  bf16x8 qr[SUB][4];
+#pragma unroll
+  for (int sb = 0; sb < SUB; ++sb) {
+    const int row = rw0 + 32 * sb + l32;
     const __bf16* src = reinterpret_cast<const __bf16*>(p.q) +
                         ((size_t)(p.q_row0[s] + row) * p.hq + head) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qr[ks] = row < Lq ? *reinterpret_cast<const bf16x8*>(src + ks * 16) : bf16x8{};
+      qr[sb][ks] = row < Lq ? *reinterpret_cast<const bf16x8*>(src + ks * 16) : bf16x8{};
   }
 
   // ---- tile copy HBM -> LDS: 16-byte slot i of a tile (lane-linear per wave and
@@ -266,22 +271,28 @@ void fwd_bf16_kernel(FwdParams p) {
     v_addr[1] += delta;
   };
 
-  f32x16 acc[2];  // O^T, [dblk]
-  acc[0] = f32x16{};
-  acc[1] = f32x16{};
-  float m_run = -INFINITY;  // reference max of this lane's query (log2 units, scaled)
-  // Exponent offset.  A row that sees no key keeps no reference: its offset
-  // stays +3e38, which still gives exact zeros for its -inf scores (and would
-  // overflow any visible score to +inf, sending it down the exact path).
-  float neg_m = 3.0e38f;
-  float l_run = 0.f;        // lane-partial sum of 2^(s*c - m_run)
+  // Per sub-tile: O^T accumulators [sb][dblk]; the reference max of this
+  // lane's query (log2 units, scaled); the exponent offset; the lane-partial
+  // sum of 2^(s*c - m_run).  A row that sees no key keeps no reference: its
+  // offset stays +3e38, which still gives exact zeros for its -inf scores (and
+  // would overflow any visible score to +inf, sending it down the exact path).
+  f32x16 acc[SUB][2];
+  float m_run[SUB], neg_m[SUB], l_run[SUB];
+#pragma unroll
+  for (int sb = 0; sb < SUB; ++sb) {
+    acc[sb][0] = f32x16{};
+    acc[sb][1] = f32x16{};
+    m_run[sb] = -INFINITY;
+    neg_m[sb] = 3.0e38f;
+    l_run[sb] = 0.f;
+  }
   const float c2 = p.scale_log2;
   // Make the scalar load of c2 complete here: otherwise its wait (lgkmcnt,
   // shared with LDS reads) lands inside the loop, where the first use is, and
   // drains every LDS read in flight at the top of each iteration.
   asm volatile("" ::"s"(c2));
-  f32x16 S[2];              // scores of blocks i (S[i&1]) and i+1: keys x this wave's 32 queries
-  bf16x8 P[2][2];           // bf16 probabilities of blocks i and i-1 ([i&1]), per 16-key step
+  f32x16 S[2][SUB];         // scores of blocks i (S[i&1]) and i+1 per sub-tile: keys x 32 queries
+  bf16x8 P[2][SUB][2];      // bf16 probabilities of blocks i and i-1 ([i&1]), per sub-tile and 16-key step
   bf16x8 vnext[4];          // values of the block whose O += P V comes next
 
   // K operand of 16-key step ks of block `sub` in the current key buffer
@@ -297,19 +308,21 @@ void fwd_bf16_kernel(FwdParams p) {
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * D * 2));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // exponentials of the 8 scores of 16-key step st against the current reference
-  // (-> Pst; four independent partial sums)
-  auto exps_half = [&](const f32x16& Sb, bf16x8& Pst, float* part, auto st_tag) __attribute__((always_inline)) {
+  // exponentials of the 8 scores of 16-key step ST of sub-tile SB against its
+  // current reference (-> Pst; four independent partial sums)
+  auto exps_half = [&](const f32x16& Sb, bf16x8& Pst, float* part, auto st_tag, auto sb_tag)
+      __attribute__((always_inline)) {
     constexpr int ST = decltype(st_tag)::value;
+    constexpr int SB = decltype(sb_tag)::value;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(Sb[ST * 8 + j], c2, neg_m));
+      const float pv = __builtin_amdgcn_exp2f(fmaf(Sb[ST * 8 + j], c2, neg_m[SB]));
       if (ST == 0 && j < 4) part[j] = pv; else part[j & 3] += pv;
       Pst[j] = (__bf16)pv;
     }
   };
-  auto mask = [&](f32x16& Sb, int b) __attribute__((always_inline)) {
-    const int qpos = qp0 + rw0 + l32;
+  auto mask = [&](f32x16& Sb, int b, int sb) __attribute__((always_inline)) {
+    const int qpos = qp0 + rw0 + 32 * sb + l32;
     int last = Lk - 1;
     if (p.causal) last = min(last, qpos - kp0);
     const int lim = last - b * 32 - half * 4;
@@ -326,63 +339,84 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, Sb[e]), Sb[e + 1]);
     return fmaxf(mx, Sb[15]);
   };
-  // raise the reference max of each row to the row max whose lane maxima are mx
-  // (rescaling acc and l)
-  auto raise_reference = [&](float mx) __attribute__((always_inline)) {
-    const float m_new = fmaxf(m_run, max_halves(mx) * c2);
-    if (m_new > m_run) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was -inf
-      l_run *= alpha;
-      acc[0] *= alpha;
-      acc[1] *= alpha;
-      m_run = m_new;
-      neg_m = -m_new;
+  // raise the reference max of each row of sub-tile SB to the row max whose
+  // lane maxima are mx (rescaling its acc and l)
+  auto raise_reference = [&](float mx, auto sb_tag) __attribute__((always_inline)) {
+    constexpr int SB = decltype(sb_tag)::value;
+    const float m_new = fmaxf(m_run[SB], max_halves(mx) * c2);
+    if (m_new > m_run[SB]) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run[SB] - m_new);  // 0 when m_run was -inf
+      l_run[SB] *= alpha;
+      acc[SB][0] *= alpha;
+      acc[SB][1] *= alpha;
+      m_run[SB] = m_new;
+      neg_m[SB] = -m_new;
     }
   };
-  auto settle_reference = [&](const f32x16& Sb) __attribute__((always_inline)) { raise_reference(lane_max(Sb)); };
+  // scores of block b (its keys at `kfetch`) for both sub-tiles, masked if need be
+  auto scores2 = [&](f32x16* Sb, int b, auto kfetch) __attribute__((always_inline)) {
+    Sb[0] = f32x16{};
+    Sb[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 kk = kfetch(ks);
+      Sb[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qr[0][ks], Sb[0], 0, 0, 0);
+      Sb[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qr[1][ks], Sb[1], 0, 0, 0);
+    }
+    if (b >= nfull) {
+      mask(Sb[0], b, 0);
+      mask(Sb[1], b, 1);
+    }
+  };
 
   // One step of the software pipeline for block i (i % 4 == J, compile-time).
   // The softmax of block i runs on the vector ALU while the matrix core does
-  // O += P V for block i-1 (first half) and S = K Q^T for block i+1 (second
-  // half); both are independent of block i, so one wave keeps both units fed.
+  // O += P V for block i-1 (first half, beside sub-tile 0's exponentials) and
+  // S = K Q^T for block i+1 (second half, beside sub-tile 1's); both are
+  // independent of block i, so one wave keeps both units fed.
   //
-  // Exponentials are taken against the row's current reference max and kept
+  // Exponentials are taken against each row's current reference max and kept
   // when every lane-partial row sum is <= the lane's accumulated sum (clamped
   // to [1, 2^8]), so p <= 256 and the block does not dominate the row.
-  // Otherwise - a score outgrew the reference - the block's scores are
-  // recomputed (they are not kept live: registers), the reference is raised to
-  // the row max with acc and l rescaled, and the exponentials redone.
+  // Otherwise - a score outgrew its reference, in either sub-tile - both
+  // sub-tiles' scores are recomputed (they are not kept live: registers), each
+  // reference is raised to its row max with acc and l rescaled, and the
+  // exponentials redone.
   //
-  // Buffers: block i's keys are read at step i-1 and its values at the end of
-  // step i, after the matrix work is issued, so their latency is covered by
-  // the step's tail and they are in registers when step i+1 starts.
-  // At J == 3, between the two halves, all waves meet at the tile barrier: by
-  // then every wave has read the keys of this tile and the values of the tile
-  // before it, so the next-but-one tile is copied into those buffers.  The
-  // only later read of this tile's keys would be a recompute at J == 3, which
-  // therefore reads the keys from global memory.
+  // Buffers: block i+1's keys are read at the start of the second half and
+  // block i's values at the end of the step, after the matrix work is issued,
+  // so their latency is covered by the step's tail and they are in registers
+  // when step i+1 starts.  At J == 3, between the two halves, all waves meet at
+  // the tile barrier: by then every wave has read the keys of this tile and the
+  // values of the tile before it, so the next-but-one tile is copied into those
+  // buffers.  The only later read of this tile's keys would be a recompute at
+  // J == 3, which therefore reads the keys from global memory.
   auto step = [&](auto j_tag, int i) __attribute__((always_inline)) {
     constexpr int J = decltype(j_tag)::value;
     constexpr int CUR = J & 1, NXT = CUR ^ 1;
     const bool masked = i >= nfull;  // workgroup-uniform
-    if (masked) mask(S[CUR], i);
+    if (masked) {
+      mask(S[CUR][0], i, 0);
+      mask(S[CUR][1], i, 1);
+    }
     if constexpr (J == 0) advance_v(i >> 2);
-    float part[4];
-    // ---- first half: exponentials of keys 0..15 with O += V^T P^T of block i-1
+    float part0[4], part1[4];
+    // ---- first half: exponentials of sub-tile 0 with O += V^T P^T of block i-1
     {
-      const bf16x8* va = vnext;
-      exps_half(S[CUR], P[CUR][0], part, Int<0>{});
-      {
+      exps_half(S[CUR][0], P[CUR][0][0], part0, Int<0>{}, Int<0>{});
+      exps_half(S[CUR][0], P[CUR][0][1], part0, Int<1>{}, Int<0>{});
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int db = 0; db < 2; ++db)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[2 * st + db], P[NXT][st], acc[db], 0, 0, 0);
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // exp / fma / add / convert
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        }
+          for (int sb = 0; sb < SUB; ++sb)
+            acc[sb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vnext[2 * st + db], P[NXT][sb][st],
+                                                                  acc[sb][db], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // exp / fma / add / convert
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
     }
     if constexpr (J == 3) {
@@ -395,25 +429,25 @@ void fwd_bf16_kernel(FwdParams p) {
       if ((i >> 2) + 2 < ntile) copy_tile((i >> 2) + 2);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // ---- second half: exponentials of keys 16..31 with S = K Q^T of block i+1
+    // ---- second half: exponentials of sub-tile 1 with S = K Q^T of block i+1
     {
       bf16x8 ka[4];
-      {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) ka[ks] = kread(ks, Int<(J + 1) & 3>{});
-      }
-      exps_half(S[CUR], P[CUR][1], part, Int<1>{});
-      {
-        S[NXT] = f32x16{};
+      for (int ks = 0; ks < 4; ++ks) ka[ks] = kread(ks, Int<(J + 1) & 3>{});
+      exps_half(S[CUR][1], P[CUR][1][0], part1, Int<0>{}, Int<1>{});
+      exps_half(S[CUR][1], P[CUR][1][1], part1, Int<1>{}, Int<1>{});
+      S[NXT][0] = f32x16{};
+      S[NXT][1] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          S[NXT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qr[ks], S[NXT], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // key reads
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
+        for (int sb = 0; sb < SUB; ++sb)
+          S[NXT][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qr[sb][ks], S[NXT][sb], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // key reads
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -425,49 +459,55 @@ void fwd_bf16_kernel(FwdParams p) {
       for (int db = 0; db < 2; ++db) vnext[2 * st + db] = vread(st, db, Int<J>{});
     // convert the probabilities here, before the check, so the conversions sit
     // among this step's instructions instead of trailing it
-    asm volatile("" ::"v"(P[CUR][0]), "v"(P[CUR][1]));
-    float rs = (part[0] + part[1]) + (part[2] + part[3]);
+    asm volatile("" ::"v"(P[CUR][0][0]), "v"(P[CUR][0][1]), "v"(P[CUR][1][0]), "v"(P[CUR][1][1]));
+    float rs0 = (part0[0] + part0[1]) + (part0[2] + part0[3]);
+    float rs1 = (part1[0] + part1[1]) + (part1[2] + part1[3]);
     // keep limit: the lane's accumulated sum, clamped to [1, 2^8]; the first
     // tile's blocks are all <= the reference (it is their row max), so they only
     // need the 2^8 guard (a row that saw none of them has no reference yet)
-    const float keep = __builtin_amdgcn_fmed3f(l_run, i < BPT ? SUM_LIMIT : 1.0f, SUM_LIMIT);
-    if (__builtin_amdgcn_ballot_w64(rs > keep) != 0) {  // wave-uniform, rare
-      f32x16& Sb = S[CUR];
-      Sb = f32x16{};
+    const float lo = i < BPT ? SUM_LIMIT : 1.0f;
+    const float keep0 = __builtin_amdgcn_fmed3f(l_run[0], lo, SUM_LIMIT);
+    const float keep1 = __builtin_amdgcn_fmed3f(l_run[1], lo, SUM_LIMIT);
+    if (__builtin_amdgcn_ballot_w64(rs0 > keep0 || rs1 > keep1) != 0) {  // wave-uniform, rare
+      f32x16 Sb[SUB];
       if constexpr (J == 3) {
         const int key = min(i * 32 + l32, Lk - 1);
         const unsigned off = ((unsigned)(key * kstride) + half * 8) * 2u;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          Sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kgb + off + ks * 32),
-                                                       qr[ks], Sb, 0, 0, 0);
+        scores2(Sb, i, [&](int ks) { return *reinterpret_cast<const bf16x8*>(kgb + off + ks * 32); });
       } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          Sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<J>{}), qr[ks], Sb, 0, 0, 0);
+        scores2(Sb, i, [&](int ks) { return kread(ks, Int<J>{}); });
       }
-      if (masked) mask(Sb, i);
-      settle_reference(Sb);
-      exps_half(Sb, P[CUR][0], part, Int<0>{});
-      exps_half(Sb, P[CUR][1], part, Int<1>{});
-      rs = (part[0] + part[1]) + (part[2] + part[3]);
+      raise_reference(lane_max(Sb[0]), Int<0>{});
+      raise_reference(lane_max(Sb[1]), Int<1>{});
+      exps_half(Sb[0], P[CUR][0][0], part0, Int<0>{}, Int<0>{});
+      exps_half(Sb[0], P[CUR][0][1], part0, Int<1>{}, Int<0>{});
+      exps_half(Sb[1], P[CUR][1][0], part1, Int<0>{}, Int<1>{});
+      exps_half(Sb[1], P[CUR][1][1], part1, Int<1>{}, Int<1>{});
+      rs0 = (part0[0] + part0[1]) + (part0[2] + part0[3]);
+      rs1 = (part1[0] + part1[1]) + (part1[2] + part1[3]);
       // the next block's scores are recomputed too, so they need no registers
-      // while this path runs
-      {
-        S[NXT] = f32x16{};
+      // while this path runs (its mask, if any, is applied at its own step)
+      S[NXT][0] = f32x16{};
+      S[NXT][1] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          S[NXT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<(J + 1) & 3>{}), qr[ks], S[NXT], 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kk = kread(ks, Int<(J + 1) & 3>{});
+        S[NXT][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qr[0][ks], S[NXT][0], 0, 0, 0);
+        S[NXT][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qr[1][ks], S[NXT][1], 0, 0, 0);
       }
     }
-    l_run += rs;
+    l_run[0] += rs0;
+    l_run[1] += rs1;
   };
   // ---- prologue: tile 0 landed, tile 1 in flight, scores of block 0.
   // Step 0 also multiplies the values of block 3 of tile 0 by an all-zero P
   // (there is no block -1), and the last step computes scores of a block past
   // the end from whatever the key buffer holds; both results are unused.
-  P[1][0] = bf16x8{};
-  P[1][1] = bf16x8{};
+#pragma unroll
+  for (int sb = 0; sb < SUB; ++sb) {
+    P[1][sb][0] = bf16x8{};
+    P[1][sb][1] = bf16x8{};
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) vnext[k] = bf16x8{};
   if (nblk > 0) {
@@ -478,32 +518,21 @@ void fwd_bf16_kernel(FwdParams p) {
     // the row max over the first tile is the first reference, so its blocks
     // take the kept path with every weight <= 1 (rows that see none of it keep
     // -inf); block 0's scores are computed last and stay in S[0]
+    static_assert(BPT == 4, "the first reference spans the four blocks of a tile");
+    float mx0 = -INFINITY, mx1 = -INFINITY;
     auto first_scores = [&](auto b_tag) __attribute__((always_inline)) {
       constexpr int B = decltype(b_tag)::value;
-      S[0] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, Int<B>{}), qr[ks], S[0], 0, 0, 0);
-      if (B >= nfull) mask(S[0], B);
-      return lane_max(S[0]);
+      scores2(S[0], B, [&](int ks) { return kread(ks, Int<B>{}); });
+      mx0 = fmaxf(mx0, lane_max(S[0][0]));
+      mx1 = fmaxf(mx1, lane_max(S[0][1]));
     };
-    static_assert(BPT == 4, "the first reference spans the four blocks of a tile");
-    float mx = first_scores(Int<3>{});
-    mx = fmaxf(mx, first_scores(Int<2>{}));
-    mx = fmaxf(mx, first_scores(Int<1>{}));
-    mx = fmaxf(mx, first_scores(Int<0>{}));
-    raise_reference(mx);
+    first_scores(Int<3>{});
+    first_scores(Int<2>{});
+    first_scores(Int<1>{});
+    first_scores(Int<0>{});
+    raise_reference(mx0, Int<0>{});
+    raise_reference(mx1, Int<1>{});
   }
-  // O += V^T P^T of the last block (its values were read at the end of its step)
-  auto last_pv = [&](auto j_tag, int i) __attribute__((always_inline)) {
-    constexpr int J = decltype(j_tag)::value;
-    (void)i;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vnext[2 * st + db], P[J & 1][st], acc[db], 0, 0, 0);
-  };
   if (nblk > 0) {
     for (int i0 = 0; i0 < nblk; i0 += 4) {
       step(Int<0>{}, i0);
@@ -511,58 +540,69 @@ void fwd_bf16_kernel(FwdParams p) {
       step(Int<2>{}, i0 + 2);
       step(Int<3>{}, i0 + 3);
     }
-    last_pv(Int<3>{}, 0);
+    // O += V^T P^T of the last block (its values were read at the end of its step)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb)
+          acc[sb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vnext[2 * st + db], P[1][sb][st], acc[sb][db],
+                                                                0, 0, 0);
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; written, or merged into
-  // the running state (o, lse) by their log-sum-exps (rows that saw no key here
-  // leave the state as it is)
-  const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+  // ---- epilogue, per sub-tile: O = acc / l, LSE = (m + log2 l) * ln 2; written,
+  // or merged into the running state (o, lse) by their log-sum-exps (rows that
+  // saw no key here leave the state as it is)
   // (the lane index is taken afresh from the exec mask, so no lane-derived value
   // has to stay live across the loop)
   const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int half_e = lane_e >> 5;
-  const int row = rw0 + (lane_e & 31);
-  if (row < Lq) {
-    const size_t grow = (size_t)(p.q_row0[s] + row);
-    float* dst = p.o + (grow * p.hq + head) * D + half_e * 4;
-    float* lse_dst = p.lse + (size_t)head * p.total_q + grow;
-    const float lse_b = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-    if (!p.merge) {
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+  for (int sb = 0; sb < SUB; ++sb) {
+    const float l_tot = sum_halves(l_run[sb]);
+    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    const int row = rw0 + 32 * sb + (lane_e & 31);
+    if (row < Lq) {
+      const size_t grow = (size_t)(p.q_row0[s] + row);
+      float* dst = p.o + (grow * p.hq + head) * D + half_e * 4;
+      float* lse_dst = p.lse + (size_t)head * p.total_q + grow;
+      const float lse_b = l_tot > 0.f ? (m_run[sb] + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+      if (!p.merge) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 v4;
-          v4[0] = acc[db][i * 4 + 0] * inv;
-          v4[1] = acc[db][i * 4 + 1] * inv;
-          v4[2] = acc[db][i * 4 + 2] * inv;
-          v4[3] = acc[db][i * 4 + 3] * inv;
-          *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = v4;
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4 v4;
+            v4[0] = acc[sb][db][i * 4 + 0] * inv;
+            v4[1] = acc[sb][db][i * 4 + 1] * inv;
+            v4[2] = acc[sb][db][i * 4 + 2] * inv;
+            v4[3] = acc[sb][db][i * 4 + 3] * inv;
+            *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = v4;
+          }
+        if (half_e == 0) *lse_dst = lse_b;
+      } else if (l_tot > 0.f) {
+        // the running state's O and LSE are loaded together, before the weights
+        // need the LSE (both halves read the LSE before half 0 writes it)
+        f32x4 oa[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) oa[k] = *reinterpret_cast<const f32x4*>(dst + (k >> 2) * 32 + (k & 3) * 8);
+        const float la = *lse_dst;
+        float lse, wa, wb;
+        lse_merge_weights(la, lse_b, &lse, &wa, &wb);
+        const float wbi = wb * inv;  // this block's weight times its normaliser
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int db = k >> 2, i = k & 3;
+          f32x4 o4;
+          o4[0] = fmaf(wbi, acc[sb][db][i * 4 + 0], wa * oa[k][0]);
+          o4[1] = fmaf(wbi, acc[sb][db][i * 4 + 1], wa * oa[k][1]);
+          o4[2] = fmaf(wbi, acc[sb][db][i * 4 + 2], wa * oa[k][2]);
+          o4[3] = fmaf(wbi, acc[sb][db][i * 4 + 3], wa * oa[k][3]);
+          *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = o4;
         }
-      if (half_e == 0) *lse_dst = lse_b;
-    } else if (l_tot > 0.f) {
-      // the running state's O and LSE are loaded together, before the weights
-      // need the LSE (both halves read the LSE before half 0 writes it)
-      f32x4 oa[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) oa[k] = *reinterpret_cast<const f32x4*>(dst + (k >> 2) * 32 + (k & 3) * 8);
-      const float la = *lse_dst;
-      float lse, wa, wb;
-      lse_merge_weights(la, lse_b, &lse, &wa, &wb);
-      const float wbi = wb * inv;  // this block's weight times its normaliser
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int db = k >> 2, i = k & 3;
-        f32x4 o4;
-        o4[0] = fmaf(wbi, acc[db][i * 4 + 0], wa * oa[k][0]);
-        o4[1] = fmaf(wbi, acc[db][i * 4 + 1], wa * oa[k][1]);
-        o4[2] = fmaf(wbi, acc[db][i * 4 + 2], wa * oa[k][2]);
-        o4[3] = fmaf(wbi, acc[db][i * 4 + 3], wa * oa[k][3]);
-        *reinterpret_cast<f32x4*>(dst + db * 32 + i * 8) = o4;
+        if (half_e == 0) *lse_dst = lse;
       }
-      if (half_e == 0) *lse_dst = lse;
     }
   }
 }
@@ -573,7 +613,6 @@ hipError_t launch_fwd_bf16(const FwdParams& p, const Bf16Geometry& geo, int n_un
                            hipStream_t stream) {
   const dim3 grid(n_units * p.n_head_groups), block(geo.waves * 64);
   switch (geo.heads_per_group) {
-    case 8: hipLaunchKernelGGL((fwd_bf16_kernel<8>), grid, block, 0, stream, p); break;
     case 4: hipLaunchKernelGGL((fwd_bf16_kernel<4>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((fwd_bf16_kernel<2>), grid, block, 0, stream, p); break;
     default: hipLaunchKernelGGL((fwd_bf16_kernel<1>), grid, block, 0, stream, p); break;

@@ -37,8 +37,8 @@ struct FwdParams {
 };
 
 // Tile geometry of the bf16 MFMA kernel, shared with the host planner.
-constexpr int kBf16Waves = 8;        // waves per workgroup
-constexpr int kBf16RowsPerWave = 32; // query rows per wave
+constexpr int kBf16Waves = 4;        // waves per workgroup
+constexpr int kBf16RowsPerWave = 64; // query rows per wave (two 32-row sub-tiles)
 
 struct Bf16Geometry {
   int waves;           // waves per workgroup
@@ -47,13 +47,13 @@ struct Bf16Geometry {
   int rows_per_tile() const { return rows_per_wave * (waves / heads_per_group); }
 };
 
-// Heads per workgroup: the largest of 8, 4, 2, 1 dividing the GQA group size.
+// Heads per workgroup: the largest of 4, 2, 1 dividing the GQA group size.
 inline Bf16Geometry bf16_geometry(int hq, int hkv) {
   const int group = hq / hkv;
   Bf16Geometry g;
   g.waves = kBf16Waves;
   g.rows_per_wave = kBf16RowsPerWave;
-  g.heads_per_group = (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+  g.heads_per_group = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
   return g;
 }
 

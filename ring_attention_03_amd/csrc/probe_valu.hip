@@ -47,6 +47,11 @@
 //                  (the same bytes in 8 instead of 12 reads)
 //  26 mix_lds_2tile two query sub-tiles per wave share every LDS operand:
 //                  per iteration 16 MFMAs, twice the vector work, 12 reads
+//  27 mul     v_mul_f32             8 chains
+//  28 fmamk   v_fmamk_f32 (a multiplier given as a literal) 8 chains
+//  29 fmac    v_fmac_f32 (the accumulator is the destination) 8 chains
+//  30 mix_lit      the block mix with the exponent's scale as a literal (v_fmamk_f32)
+//  31 mix_lds_lit  the LDS-fed block mix (23) with the scale as a literal
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,6 +89,12 @@ __device__ __forceinline__ float vector_probe(int iters) {
         } else if constexpr (MODE == 3) {
           // (written out so no repacking instructions surround it)
           asm volatile("v_cvt_pk_bf16_f32 %0, %0, %1" : "+v"(x[c]) : "v"(a));
+        } else if constexpr (MODE == 27) {
+          x[c] = x[c] * a;
+        } else if constexpr (MODE == 28) {
+          x[c] = fmaf(x[c], 0.18033688f, b);
+        } else if constexpr (MODE == 29) {
+          x[c] = fmaf(a, b, x[c]);
         } else if constexpr (MODE == 4) {
           const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
           x[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, __float_as_uint(b)), ones, x[c], false);
@@ -97,6 +108,20 @@ __device__ __forceinline__ float vector_probe(int iters) {
 #pragma unroll
   for (int c = 0; c < CH; ++c) s += x[c];
   return s;
+}
+
+// x * scale + shift; with LIT the scale is the literal log2(e)/8 in a v_fmamk_f32
+// (written out: with the literal used many times the compiler keeps it in a
+// register and emits v_fma_f32)
+template <bool LIT>
+__device__ __forceinline__ float scale_shift(float x, float scale, float shift) {
+  if constexpr (LIT) {
+    float r;
+    asm("v_fmamk_f32 %0, %1, 0x3e38aa3b, %2" : "=v"(r) : "v"(x), "v"(shift));
+    return r;
+  } else {
+    return fmaf(x, scale, shift);
+  }
 }
 
 template <int MODE>
@@ -146,6 +171,7 @@ __device__ __forceinline__ float mix_probe(int iters) {
   constexpr int NFMA = MODE == 13 ? 8 : 4;
   constexpr bool ONLY_EXP = MODE == 12;
   constexpr bool POLY = MODE == 15;
+  constexpr bool LIT = MODE == 30;  // the scale as a compile-time literal
   // matrix work: 0 = 8 x 32x32x16 (VGPR accumulators), 1 = 16 x 16x16x32, 2 = 8 x 32x32x16 in AGPRs
   // 3 = A, B, C in AGPRs; 4 = A, C in AGPRs
   constexpr int MK = (MODE == 16 || MODE == 19) ? 1 : (MODE == 17 || MODE == 18) ? 2
@@ -190,7 +216,7 @@ __device__ __forceinline__ float mix_probe(int iters) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int i = 2 * k + j;
-          f[i] = fmaf(s[i], cs, nm);
+          f[i] = scale_shift<LIT>(s[i], cs, nm);
           if constexpr (POLY) {
             // 2^x = 2^n * 2^r, n = round(x), r in [-1/2, 1/2]: the magic constant
             // rounds x into the low mantissa bits of t; cubic in r
@@ -211,8 +237,8 @@ __device__ __forceinline__ float mix_probe(int iters) {
       if constexpr (MF && MK >= 2) __builtin_amdgcn_sched_barrier(0);  // (asm is not a schedule group)
       if constexpr (MF && MK < 2) {
         __builtin_amdgcn_sched_group_barrier(0x008, MK == 1 ? 2 : 1, 0);  // the MFMA(s)
-        __builtin_amdgcn_sched_group_barrier(0x002, ONLY_FMA ? NFMA : ONLY_EXP ? 2 : POLY ? 23 : (EX ? 7 : 5),
-                                             0);  // its vector share
+        __builtin_amdgcn_sched_group_barrier(0x002, ONLY_FMA ? NFMA : ONLY_EXP ? 2 : POLY ? 23 : LIT ? 5 : (EX ? 7 : 5),
+                                             0);  // its vector share (the literal FMAs are asm: not counted)
       }
     }
   }
@@ -229,7 +255,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // The block mix fed from LDS like the attention kernel: per iteration 4 A
 // operands by ds_read_b128 (keys) and 8 half-operands by ds_read_b64_tr_b16
 // (values), addresses inside the 16 KiB at `lds`.
-template <bool FEED, bool VB128 = false, int TILES = 1>
+template <bool FEED, bool VB128 = false, int TILES = 1, bool LIT = false>
 __device__ __forceinline__ float mix_lds_probe(int iters, const __attribute__((address_space(3))) char* lds) {
   bf16x8 r1, r2;
 #pragma unroll
@@ -276,14 +302,14 @@ __device__ __forceinline__ float mix_lds_probe(int iters, const __attribute__((a
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int i = 2 * kk + j;
-        e[i] = __builtin_amdgcn_exp2f(fmaf(s[i], cs, tl ? nm2 : nm));
+        e[i] = __builtin_amdgcn_exp2f(scale_shift<LIT>(s[i], cs, tl ? nm2 : nm));
         acc[i & 3] += e[i];
       }
       const bf16x2 p2 = {(__bf16)e[2 * kk], (__bf16)e[2 * kk + 1]};
       pk[kk] = __builtin_bit_cast(unsigned, p2);
       asm volatile("" ::"v"(pk[kk]));
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, LIT ? 5 : 7, 0);
     }
   }
   float t = acc[0] + acc[1] + acc[2] + acc[3] + c[0][0] + c[1][5] + c[2 * TILES - 1][3];
@@ -300,11 +326,11 @@ __global__ __launch_bounds__(1024) void probe_valu_kernel(float* sink, unsigned 
   const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   float r;
-  if constexpr (MODE <= 5) {
+  if constexpr (MODE <= 5 || (MODE >= 27 && MODE <= 29)) {
     r = vector_probe<MODE>(iters);
   } else if constexpr (MODE <= 7) {
     r = matrix_probe<MODE>(iters);
-  } else if constexpr (MODE >= 23 && MODE <= 26) {
+  } else if constexpr ((MODE >= 23 && MODE <= 26) || MODE == 31) {
     // 16 KiB of this workgroup's LDS as the operand source (contents arbitrary but finite)
     const int tid = __builtin_amdgcn_workitem_id_x();
     for (int i = tid; i < 4096; i += __builtin_amdgcn_workgroup_size_x()) pad[i] = 0.001f * (float)(i & 255);
@@ -314,6 +340,8 @@ __global__ __launch_bounds__(1024) void probe_valu_kernel(float* sink, unsigned 
       r = mix_lds_probe<true, true>(iters, lds);
     else if constexpr (MODE == 26)
       r = mix_lds_probe<true, false, 2>(iters, lds);
+    else if constexpr (MODE == 31)
+      r = mix_lds_probe<true, false, 1, true>(iters, lds);
     else
       r = mix_lds_probe<MODE == 23>(iters, lds);
   } else {
@@ -344,7 +372,7 @@ hipError_t launch(float* sink, unsigned long long* cycles, unsigned long long* r
 
 // Instructions of each probe per loop iteration (per wave), for the host's arithmetic:
 // vector probes 32 (4 unrolled x 8 chains); matrix probes 16 MFMAs; mix probes one block.
-extern "C" int attn_probe_valu_modes(void) { return 27; }
+extern "C" int attn_probe_valu_modes(void) { return 32; }
 
 // Run probe `mode` on `cus` CUs with `waves_per_simd` (1, 2 or 4) waves per
 // SIMD for `iters` iterations: cus workgroups of 256 * waves_per_simd threads.
@@ -388,6 +416,11 @@ extern "C" int attn_probe_valu(float* sink, unsigned long long* cycles, unsigned
     case 24: e = launch<24>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
     case 25: e = launch<25>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
     case 26: e = launch<26>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 27: e = launch<27>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 28: e = launch<28>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 29: e = launch<29>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 30: e = launch<30>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 31: e = launch<31>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)e;

@@ -48,19 +48,19 @@ def last():
     return cnt, n.value, m.value, list(off[: s.value + 1])
 
 flag = ctypes.c_int32(-1)
-# a visible block launches: 128 rows at 8:1 GQA = 4 row tiles of 32 rows
+# a visible block launches: 128 rows at 8:1 GQA = 2 row tiles of 64 rows (4 heads x 64 rows per workgroup)
 p, keep = problem()
 assert lib.attn_ring_step(ctypes.byref(p), 0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, ctypes.byref(flag), None) == 0
 assert flag.value == 1
 cnt, units, merge, off = last()
-assert (cnt, units, merge, off) == (1, 4, 0, [0, 4]), (cnt, units, merge, off)
+assert (cnt, units, merge, off) == (1, 2, 0, [0, 2]), (cnt, units, merge, off)
 # the fused step sets the merge flag
 assert lib.attn_ring_step_merge(ctypes.byref(p), 0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None) == 0
-assert last()[:3] == (2, 4, 1)
+assert last()[:3] == (2, 2, 1)
 # varlen: the heaviest sequence is planned first (unit prefix over that order)
 p, keep = problem(num_seqs=3, total_q=96, total_k=96, cu_q=[0, 10, 80, 96], cu_k=[0, 10, 80, 96])
 assert lib.attn_prefill_causal(ctypes.byref(p), 0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None) == 0
-assert last()[1:] == (5, 0, [0, 3, 4, 5]), last()
+assert last()[1:] == (4, 0, [0, 2, 3, 4]), last()
 # a fully masked block records nothing
 p, keep = problem(q_pos0=[0], k_pos0=[500])
 assert lib.attn_ring_step(ctypes.byref(p), 0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, ctypes.byref(flag), None) == 0
