@@ -24,8 +24,8 @@
 // and S = K Q^T of block i+1 (matrix cores), which do not depend on it: the
 // first half of a step exponentiates sub-tile 0 beside O += P V of both
 // sub-tiles, the second half sub-tile 1 beside S = K Q^T of both.  Keys of
-// block i+1 are read from LDS at the start of the second half and values of
-// block i at the end of the step (held in registers for the next step's
+// block i+1 are read from LDS at the start of the step and values of block i
+// at the end of it (held in registers for the next step's
 // O += P V), so values live one tile longer than keys: LDS holds two key
 // buffers and three value buffers (80 KiB), and one barrier per tile separates
 // the copy of tile t+2 from the last reads of the buffers it reuses.
@@ -383,8 +383,9 @@ void fwd_bf16_kernel(FwdParams p) {
   // reference is raised to its row max with acc and l rescaled, and the
   // exponentials redone.
   //
-  // Buffers: block i+1's keys are read at the start of the second half and
-  // block i's values at the end of the step, after the matrix work is issued,
+  // Buffers: block i+1's keys are read at the start of the step (of the second
+  // half at J == 3) and block i's values at the end of the step, after the
+  // matrix work is issued,
   // so their latency is covered by the step's tail and they are in registers
   // when step i+1 starts.  At J == 3, between the two halves, all waves meet at
   // the tile barrier: by then every wave has read the keys of this tile and the
@@ -401,6 +402,13 @@ void fwd_bf16_kernel(FwdParams p) {
     }
     if constexpr (J == 0) advance_v(i >> 2);
     float part0[4], part1[4];
+    // keys of block i+1, read before the first half (at J == 3 they sit in the
+    // next tile, which the barrier between the halves publishes)
+    bf16x8 ka[4];
+    if constexpr (J != 3) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ka[ks] = kread(ks, Int<(J + 1) & 3>{});
+    }
     // ---- first half: exponentials of sub-tile 0 with O += V^T P^T of block i-1
     {
       exps_half(S[CUR][0], P[CUR][0][0], part0, Int<0>{}, Int<0>{});
@@ -415,7 +423,7 @@ void fwd_bf16_kernel(FwdParams p) {
                                                                   acc[sb][db], 0, 0, 0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // exp / fma / add / convert
+        __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // exp / fma / add / convert
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
     }
@@ -431,9 +439,10 @@ void fwd_bf16_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     // ---- second half: exponentials of sub-tile 1 with S = K Q^T of block i+1
     {
-      bf16x8 ka[4];
+      if constexpr (J == 3) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) ka[ks] = kread(ks, Int<(J + 1) & 3>{});
+        for (int ks = 0; ks < 4; ++ks) ka[ks] = kread(ks, Int<(J + 1) & 3>{});
+      }
       exps_half(S[CUR][1], P[CUR][1][0], part1, Int<0>{}, Int<1>{});
       exps_half(S[CUR][1], P[CUR][1][1], part1, Int<1>{}, Int<1>{});
       S[NXT][0] = f32x16{};
@@ -443,10 +452,10 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb)
           S[NXT][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qr[sb][ks], S[NXT][sb], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // key reads
+      if constexpr (J == 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // key reads
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     }
