@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import platform
 import sys
@@ -190,7 +191,32 @@ class Job:
                 "merge": "in the step kernel" if self.fused else "separate merge kernel"}
 
 
-def time_job(job, steps, warmup):
+def warm_up(job, warmup, min_seconds=0.0):
+    """Run `warmup` untimed steps, then more until about `min_seconds` have passed.
+
+    Returns the number of steps run.  After the host-side setup of a workload
+    the GPU has idled, and its clock takes tens of milliseconds of load to
+    settle (a 32K ring step ran 8% slow over its first 20 ms), so a workload
+    with short steps needs more than a few steps of warmup.
+    """
+    import torch
+
+    t0 = time.perf_counter()
+    for _ in range(warmup):
+        job.run()
+    torch.cuda.synchronize()
+    done = warmup
+    elapsed = time.perf_counter() - t0
+    if warmup > 0 and elapsed < min_seconds:
+        more = int(math.ceil((min_seconds - elapsed) / (elapsed / warmup)))
+        for _ in range(more):
+            job.run()
+        torch.cuda.synchronize()
+        done += more
+    return done
+
+
+def time_job(job, steps, warmup, min_warmup_seconds=0.0):
     """Median-free whole-job timing: warmup, then exactly `steps` steps between synchronizations.
 
     The wall-clock region behind the throughput holds only the launches.  The
@@ -198,12 +224,12 @@ def time_job(job, steps, warmup):
     right after it, with HIP events recorded around every launch on the
     launch stream: each event is a packet of its own in the stream, which adds
     a few microseconds between launches, so it is kept out of the first region.
+    `min_warmup_seconds` extends the warmup (see `warm_up`); the headline run
+    uses exactly the requested warmup steps.
     """
     import torch
 
-    for _ in range(warmup):
-        job.run()
-    torch.cuda.synchronize()
+    job.warmup_steps_run = warm_up(job, warmup, min_warmup_seconds)
     t0 = time.perf_counter()
     for _ in range(steps):
         job.run()
@@ -720,9 +746,10 @@ def main():
     for name in [x for x in args.extra.split(",") if x and x != args.workload]:
         log(f"bench: preparing {name}")
         ej = Job(name, fused=not args.unfused)
-        ew, epk = time_job(ej, args.extra_steps, args.extra_warmup)
+        ew, epk = time_job(ej, args.extra_steps, args.extra_warmup, min_warmup_seconds=0.3)
         extra[name] = summarize(ej, args.extra_steps, ew, epk)
         extra[name]["algorithmic_tflop"] = ej.flops / 1e12
+        extra[name]["warmup_steps"] = ej.warmup_steps_run
         log(f"bench: {name}: {extra[name]['ms_per_step']:.3f} ms/step, {extra[name]['tflops']:.1f} TFLOP/s")
         del ej
         torch.cuda.empty_cache()

@@ -127,3 +127,29 @@ def test_trace_summary_lists_the_warmup_apart(tmp_path, capsys):
     assert abs(rec["kernel_ms_per_step"] - 6.0) < 1e-12
     flop = 4 * 64 * 64 * (lambda c: sum(range(7 * c + 1, 8 * c + 1)))(8192) / per_step
     assert rec["flop_per_launch"] == flop
+
+
+class _FakeJob:
+    """A job whose steps take `dt` seconds of host time (no GPU)."""
+
+    def __init__(self, dt):
+        self.dt, self.steps = dt, 0
+
+    def run(self):
+        self.steps += 1
+        import time as _t
+        _t.sleep(self.dt)
+
+
+def test_warmup_extends_to_a_minimum_time(monkeypatch):
+    bench = _load_bench()
+    import types
+    fake_torch = types.SimpleNamespace(cuda=types.SimpleNamespace(synchronize=lambda: None))
+    monkeypatch.setitem(sys.modules, "torch", fake_torch)
+    job = _FakeJob(0.002)
+    n = bench.warm_up(job, 5, min_seconds=0.05)
+    assert n == job.steps and 5 < n <= 40            # 5 requested, then enough for ~50 ms
+    job = _FakeJob(0.002)
+    assert bench.warm_up(job, 5) == 5 == job.steps     # no minimum: exactly the requested steps
+    job = _FakeJob(0.02)
+    assert bench.warm_up(job, 5, min_seconds=0.05) == 5  # already past the minimum

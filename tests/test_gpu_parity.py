@@ -99,6 +99,10 @@ RING_CASES = [
     ((640, 64, 192), 2, 16, 2, "normal"),        # varlen with a short sequence
     ((768,), 4, 12, 2, "uniform"),       # GQA 6:1: two heads per workgroup
     ((512,), 2, 12, 4, "normal"),        # GQA 3:1: one head per workgroup, kv head = head / 3
+    # 16 head groups: each XCD's workgroups take a contiguous range of them
+    ((640,), 2, 64, 8, "normal"),        # GQA 8:1 at the long workloads' 64/8 heads
+    ((512,), 2, 32, 16, "uniform"),      # GQA 2:1, two heads per workgroup
+    ((384,), 2, 16, 16, "normal"),       # MHA, one head per workgroup
 ]
 
 
