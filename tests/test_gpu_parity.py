@@ -541,6 +541,20 @@ def test_full_size_ring_sampled_rows(name, nsample):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("name", ["ring_32k_rank3", "ring_64k_rank7", "varlen_ulysses_rank7"])
+def test_full_size_ring_every_row(name):
+    """A full-size ring share (C2, C3, C5) against the oracle on every local row and head."""
+    from oracle_pool import ring_ref_rows
+
+    w = WORKLOADS[name]
+    log(f"full-size {name}, every row: generating inputs")
+    q, k, v = make_qkv(w)
+    o, lse = run_ring(q, k, v, w.seqlens, w.n_chunks, w.rank)
+    log(f"full-size {name}: oracle on all {o.shape[0]} rows (worker pool)")
+    o_ref, lse_ref = ring_ref_rows(name, np.arange(o.shape[0]))
+    assert_close(o, lse, o_ref, lse_ref, O_TOL_BF16, LSE_TOL_BF16, f"{name} every row")
+
+
 def test_full_size_chunked_prefill_sampled_rows():
     w = WORKLOADS["chunked_prefill_12k"]
     log("full-size chunked_prefill_12k: generating inputs")
