@@ -67,6 +67,9 @@ def parse_args():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only measure the sustained rate of back-to-back bf16 MFMAs on constant and on "
                          "random operands (the probe library built beside the attention library)")
+    ap.add_argument("--mix-ceiling", action="store_true",
+                    help="only measure the sustained matrix-core rate of the attention kernel's inner-loop "
+                         "instruction mix on constant and on random operands (the probe library)")
     ap.add_argument("--valu-rates", action="store_true",
                     help="only measure issue rates of the softmax's vector instructions and their overlap "
                          "with the matrix cores (the probe library built beside the attention library)")
@@ -584,7 +587,68 @@ VALU_PROBES = [
     ("v_mul_f32", 0, 32), ("v_fmamk_f32 (literal multiplier)", 0, 32), ("v_fmac_f32", 0, 32),
     ("block_mix_literal_scale: the block mix with its FMAs as v_fmamk_f32", 8, 56),
     ("block_mix_lds_literal_scale: the LDS-fed block mix with its FMAs as v_fmamk_f32", 8, 56),
+    ("block_mix_lds_2tiles_random: probe 26 on random bf16 operands (per-block figures)", 16, 112),
 ]
+MIX_2TILE, MIX_2TILE_RANDOM = 26, 32  # the kernel's inner loop: both query sub-tiles, LDS-fed
+
+
+def mix_ceiling():
+    """Sustained matrix-core rate of the attention kernel's inner-loop mix.
+
+    Probes 26 and 32 of the probe library: per iteration a wave does what one
+    kernel step does for its two 32-row query sub-tiles - 16 MFMAs 32x32x16
+    with their key and value operands read from LDS as the kernel reads them,
+    32 exponentials with their FMAs, 32 adds and 16 bf16 packs - on constant
+    operands (26) or random ones (32, bf16 uniform in (-2, 2)).  One workgroup
+    per CU with w waves per SIMD (2 is the kernel's occupancy).  Each case runs
+    for 3 s first, so the clock settles under its own load, then 5 launches of
+    about 0.2 s are timed.  The MFMA flops per second of that loop are what the
+    kernel would reach if it did nothing but its inner loop: no tile copies,
+    barriers, masks, keep checks, prologues, epilogues or launch ends.
+    """
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "ring_attention_03_amd", "libattnprobe.so"))
+    lib.attn_probe_valu.restype = ctypes.c_int
+    lib.attn_probe_valu.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.empty(cus * 4 * 256, device="cuda:0")
+    cyc, rt, st0 = (torch.empty(cus * 16, dtype=torch.int64, device="cuda:0") for _ in range(3))
+    for mode, operands in ((MIX_2TILE, "constant"), (MIX_2TILE_RANDOM, "random")):
+        for w in (2, 4):
+            iters = 240_000 // w
+
+            def launch():
+                rc = lib.attn_probe_valu(*(ctypes.c_void_p(t.data_ptr()) for t in (sink, cyc, rt, st0)),
+                                         mode, cus, w, iters, stream)
+                if rc != 0:
+                    raise RuntimeError(f"attn_probe_valu mode {mode} failed with HIP error {rc}")
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 3.0:
+                launch()
+                torch.cuda.synchronize()
+            reps = 5
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                launch()
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e) / reps
+            n = cus * 4 * w
+            ticks, real = cyc[:n].double(), rt[:n].double()
+            simd_per_iter = float(ticks.view(cus, 4 * w).max(dim=1).values.median()) / (iters * w)
+            flops = n * iters * 16 * 2.0 * 32 * 32 * 16
+            tf = flops / (ms * 1e-3) / 1e12
+            print(json.dumps({"mix": "attention inner loop: 16 MFMA 32x32x16 + 32 exp + 32 fma + 32 add + "
+                                     "16 cvt per wave-iteration, LDS-fed", "operands": operands,
+                              "waves_per_simd": w, "ms": round(ms, 3), "tflops": round(tf, 1),
+                              "pct_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+                              "clock_ghz": round(float((ticks / (real * 1e-8)).median()) / 1e9, 3),
+                              "mfma_busy": round(32.0 * 16 / simd_per_iter, 3)}), flush=True)
 
 
 
@@ -726,6 +790,9 @@ def main():
         return
     if args.valu_rates:
         valu_rates()
+        return
+    if args.mix_ceiling:
+        mix_ceiling()
         return
     from ring_attention_03_amd import load_library
 

@@ -52,6 +52,10 @@
 //  29 fmac    v_fmac_f32 (the accumulator is the destination) 8 chains
 //  30 mix_lit      the block mix with the exponent's scale as a literal (v_fmamk_f32)
 //  31 mix_lds_lit  the LDS-fed block mix (23) with the scale as a literal
+//  32 mix_lds_2tile_random  probe 26 on random operands: the LDS tile, the query
+//                  operands and the scores drawn from a counter hash (bf16
+//                  operands uniform in (-2, 2)), so the matrix cores draw the
+//                  power of real data and the board sets its clock accordingly
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,6 +71,19 @@ constexpr int CH = 8;  // independent chains of the vector probes
 
 __device__ __forceinline__ float lane_value(int salt) {
   return 0.25f + 0.001f * (float)((__builtin_amdgcn_workitem_id_x() * 7 + salt) & 127);
+}
+
+__device__ __forceinline__ uint32_t hash32(uint32_t x) {  // xorshift-multiply rounds
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+// uniform in (lo, lo + width) from the hash of counter `n`
+__device__ __forceinline__ float hashed_value(uint32_t n, float lo, float width) {
+  return lo + (float)(hash32(n) >> 8) * (width / 16777216.0f);
 }
 
 template <int MODE>
@@ -255,13 +272,16 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // The block mix fed from LDS like the attention kernel: per iteration 4 A
 // operands by ds_read_b128 (keys) and 8 half-operands by ds_read_b64_tr_b16
 // (values), addresses inside the 16 KiB at `lds`.
-template <bool FEED, bool VB128 = false, int TILES = 1, bool LIT = false>
+template <bool FEED, bool VB128 = false, int TILES = 1, bool LIT = false, bool RND = false>
 __device__ __forceinline__ float mix_lds_probe(int iters, const __attribute__((address_space(3))) char* lds) {
+  // with RND the query operands and the scores are random, per thread of the grid
+  const uint32_t gid = __builtin_amdgcn_workgroup_id_x() * __builtin_amdgcn_workgroup_size_x() +
+                       __builtin_amdgcn_workitem_id_x();
   bf16x8 r1, r2;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    r1[j] = (__bf16)lane_value(j + 8);
-    r2[j] = (__bf16)lane_value(j + 9);
+    r1[j] = (__bf16)(RND ? hashed_value(gid * 64u + j, -2.f, 4.f) : lane_value(j + 8));
+    r2[j] = (__bf16)(RND ? hashed_value(gid * 64u + 8 + j, -2.f, 4.f) : lane_value(j + 9));
   }
   const int lane = __builtin_amdgcn_workitem_id_x() & 63;
   // lane-linear addresses: conflict-free, like the kernel's swizzled tile reads
@@ -270,7 +290,7 @@ __device__ __forceinline__ float mix_lds_probe(int iters, const __attribute__((a
   f32x16 c[2 * TILES] = {};
   float s[16], e[16], acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) s[j] = lane_value(j + 20);
+  for (int j = 0; j < 16; ++j) s[j] = RND ? hashed_value(gid * 64u + 16 + j, -8.f, 8.f) : lane_value(j + 20);
   unsigned pk[8];
   const float cs = lane_value(50), nm = -lane_value(51), nm2 = -lane_value(52);
   for (int it = 0; it < iters; ++it) {
@@ -330,10 +350,20 @@ __global__ __launch_bounds__(1024) void probe_valu_kernel(float* sink, unsigned 
     r = vector_probe<MODE>(iters);
   } else if constexpr (MODE <= 7) {
     r = matrix_probe<MODE>(iters);
-  } else if constexpr ((MODE >= 23 && MODE <= 26) || MODE == 31) {
-    // 16 KiB of this workgroup's LDS as the operand source (contents arbitrary but finite)
+  } else if constexpr ((MODE >= 23 && MODE <= 26) || MODE == 31 || MODE == 32) {
+    // 16 KiB of this workgroup's LDS as the operand source (contents arbitrary but
+    // finite; for probe 32, pairs of random bf16 in (-2, 2))
     const int tid = __builtin_amdgcn_workitem_id_x();
-    for (int i = tid; i < 4096; i += __builtin_amdgcn_workgroup_size_x()) pad[i] = 0.001f * (float)(i & 255);
+    const uint32_t salt = 0x10000u * (1u + __builtin_amdgcn_workgroup_id_x());
+    for (int i = tid; i < 4096; i += __builtin_amdgcn_workgroup_size_x()) {
+      if constexpr (MODE == 32) {
+        const bf16x2 two = {(__bf16)hashed_value(salt + 2 * i, -2.f, 4.f),
+                            (__bf16)hashed_value(salt + 2 * i + 1, -2.f, 4.f)};
+        pad[i] = __builtin_bit_cast(float, two);
+      } else {
+        pad[i] = 0.001f * (float)(i & 255);
+      }
+    }
     __syncthreads();
     const auto* lds = (const __attribute__((address_space(3))) char*)(const __attribute__((address_space(3))) float*)pad;
     if constexpr (MODE == 25)
@@ -342,6 +372,8 @@ __global__ __launch_bounds__(1024) void probe_valu_kernel(float* sink, unsigned 
       r = mix_lds_probe<true, false, 2>(iters, lds);
     else if constexpr (MODE == 31)
       r = mix_lds_probe<true, false, 1, true>(iters, lds);
+    else if constexpr (MODE == 32)
+      r = mix_lds_probe<true, false, 2, false, true>(iters, lds);
     else
       r = mix_lds_probe<MODE == 23>(iters, lds);
   } else {
@@ -372,7 +404,7 @@ hipError_t launch(float* sink, unsigned long long* cycles, unsigned long long* r
 
 // Instructions of each probe per loop iteration (per wave), for the host's arithmetic:
 // vector probes 32 (4 unrolled x 8 chains); matrix probes 16 MFMAs; mix probes one block.
-extern "C" int attn_probe_valu_modes(void) { return 32; }
+extern "C" int attn_probe_valu_modes(void) { return 33; }
 
 // Run probe `mode` on `cus` CUs with `waves_per_simd` (1, 2 or 4) waves per
 // SIMD for `iters` iterations: cus workgroups of 256 * waves_per_simd threads.
@@ -421,6 +453,7 @@ extern "C" int attn_probe_valu(float* sink, unsigned long long* cycles, unsigned
     case 29: e = launch<29>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
     case 30: e = launch<30>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
     case 31: e = launch<31>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
+    case 32: e = launch<32>(sink, cycles, realtime, starts, cus, w, iters, stream); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)e;
